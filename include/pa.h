@@ -1,0 +1,218 @@
+/*
+ * pa.h - paged GQA attention over a block-table KV cache, for AMD MI355X (gfx950).
+ *
+ * C ABI of libpa.so. Every entry point takes plain pointers and sizes; no
+ * framework types cross this boundary. Three operations make up the path:
+ *
+ *   pa_store_kv        write new K/V rows into the paged pool through slot_mapping
+ *                      (optionally quantising them to FP8 e4m3 with per-token-per-head
+ *                      scales);
+ *   pa_decode          one query token per sequence attends its whole cached context,
+ *                      read block by block through block_tables, with an online
+ *                      softmax; long contexts are split and merged by log-sum-exp;
+ *   pa_varlen_prefill  a flat batch of query chunks (cu_seqlens) attends, causally, the
+ *                      cached prefix plus the chunk itself, per sequence.
+ *
+ * Sources (web pages; cited below by tag and section):
+ *   [P1] lvyufeng.github.io/PocketLLM .../phase3_3_completion_summary
+ *        "Phase 3.3 completion summary - Slot ID Threading and Batch API Integration"
+ *   [P2] lvyufeng.github.io/PocketLLM .../cpp_engine_batching_phase3_1
+ *        "cpp_engine Batching Implementation (Phase 3.1)"
+ *   [P4] koas-w.github.io/posts/20260331-errorsandsolutions
+ *        (milestone log, "KV Cache management", "hand-written Triton kernels",
+ *         "errors encountered", types 1-5)
+ *   [P5] happydog-intj.github.io/mini-vllm-tutorial/step14_7_batched_forward
+ *        "step14_7 - Batched Forward" ("varlen batch", "cu_seqlens is only needed in
+ *         attention", "comparison with vLLM")
+ *
+ * Conventions shared by all calls
+ * --------------------------------
+ *  - Every array argument is a DEVICE pointer owned by the caller. The library never
+ *    allocates, frees or caches device memory and keeps no global mutable state: all
+ *    addressing is passed explicitly on every call, as [P1] "design decisions /
+ *    explicit parameter passing" argues against a hidden current slot.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
+ *    default stream). They return after enqueueing and never synchronise.
+ *  - Element strides are in ELEMENTS, not bytes; the innermost (head_dim) stride is
+ *    always 1. Passing strides is how non-contiguous K/V views are handled, the fix
+ *    [P4] "errors, type 2" reports for its store kernel.
+ *  - The KV pool layout is [num_blocks, block_size, kv_heads, head_dim], dense, the
+ *    per-slot layout of [P2] "current KV cache structure" ([max_seq_len, kv_heads,
+ *    head_dim]) cut into block_size-token blocks ([P4] "KV Cache management":
+ *    16-token blocks). Physical token slot of logical position j of sequence s:
+ *        slot = block_tables[s][j / block_size] * block_size + j % block_size.
+ *  - GQA: query head h reads KV head h / (q_heads / kv_heads) (contiguous groups).
+ *  - Indices: block_tables, context_lens, cu_seqlens are int32; slot_mapping is int64.
+ *    Kernels use 64-bit element offsets, so pools may exceed 2^31 elements.
+ *  - context_lens[s] counts every token already stored for sequence s, INCLUDING the
+ *    tokens of the current step, which must be stored before attention runs ([P4]
+ *    "errors, type 1": a context length one short hides the new token from itself).
+ *  - Supported: block_size 16; head_dim 64 or 128; q_heads / kv_heads in 1..8.
+ *    dtypes: (q F32, pool F32), (q BF16, pool BF16), (q BF16, pool FP8_E4M3).
+ *  - Validation happens on the host before any launch; a failing call launches
+ *    nothing and returns a negative status. Device-data preconditions (block ids in
+ *    range, 1 <= context_lens[s] <= max_context_len, n_s <= context_lens[s]) are the
+ *    caller's contract; the kernels skip out-of-range block ids and slots rather than
+ *    touch memory outside the pool, and the affected outputs are then unspecified.
+ *  - Concurrent calls on different streams are safe when their outputs (and
+ *    workspaces) are disjoint.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+enum {
+  PA_F32 = 0,      /* IEEE binary32 */
+  PA_BF16 = 1,     /* bfloat16 */
+  PA_FP8_E4M3 = 2  /* OCP e4m3fn codes (bias 7, max 448, no infinities), KV pools only */
+};
+
+/* Status codes. */
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad stride, bad dtype combo */
+  PA_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, block_size, group size */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_bytes() */
+  PA_ERR_HIP = -4          /* a kernel launch failed */
+};
+
+/* One layer's KV pool. Caller-owned, dense, persists across calls (it is the cache).
+ *   k, v       [num_blocks, block_size, kv_heads, head_dim] of `dtype`
+ *   k_scale,   [num_blocks, block_size, kv_heads] fp32; required iff dtype is
+ *   v_scale    PA_FP8_E4M3 (per-token-per-head dequantisation scales, the
+ *              k_scale/v_scale "used for FP8/INT8 quantisation" of [P2]), else NULL. */
+typedef struct pa_kv_pool {
+  void *k;
+  void *v;
+  float *k_scale;
+  float *v_scale;
+  int64_t num_blocks;
+  int32_t block_size;
+  int32_t kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+} pa_kv_pool_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *pa_status_string(int status);
+
+/*
+ * pa_store_kv - scatter new K/V rows into the pool through slot_mapping.
+ *
+ * Defined by [P4] "hand-written Triton kernels" (store_kvcache_kernel: a token x head
+ * grid writes each new K/V row directly to its physical cache slot, with strides for
+ * non-contiguous inputs) and [P2] "Step 3.4" (append of `rows` new K/V rows at an
+ * offset into a slot's contiguous cache, the special case slot = slot_id*max_len+pos).
+ *
+ *   k, v            new rows, [num_tokens, kv_heads, head_dim] of src_dtype with
+ *                   element strides (k_stride_tok, k_stride_head) and
+ *                   (v_stride_tok, v_stride_head); innermost stride 1.
+ *   slot_mapping    [num_tokens] int64 physical slots. slot < 0 means "skip this token"
+ *                   (padding). Slots >= num_blocks*block_size are skipped too.
+ *                   Two tokens with the same slot in one call is a contract violation.
+ *   For t with a valid slot and every head g < kv_heads:
+ *     pool->dtype == src_dtype (F32 or BF16): the row is copied bit for bit to
+ *         pool->k[slot / block_size][slot % block_size][g][:] (same for v).
+ *     pool->dtype == PA_FP8_E4M3 (src_dtype F32 or BF16): per row x (fp32 values),
+ *         a = max_d |x_d|; scale = a / 448 (fp32, correctly rounded);
+ *         code_d = e4m3fn(x_d / scale) with round-to-nearest-even and saturation to
+ *         +-448; a == 0 gives scale 0 and all codes 0x00. Codes go to the pool, the
+ *         scale to pool->k_scale[slot / block_size][slot % block_size][g] (same for v).
+ *         Source values must be finite.
+ *   Every byte of the pool not named by a valid slot is left untouched.
+ *   num_tokens == 0 is a no-op returning PA_OK.
+ */
+int pa_store_kv(const pa_kv_pool_t *pool, const void *k, const void *v, int32_t src_dtype,
+                int64_t num_tokens, int64_t k_stride_tok, int64_t k_stride_head,
+                int64_t v_stride_tok, int64_t v_stride_head, const int64_t *slot_mapping,
+                void *stream);
+
+/*
+ * pa_decode_workspace_bytes - bytes of device workspace pa_decode needs for these
+ * sizes and this split length (0 when no context can need more than one split).
+ * Returns 0 for invalid arguments as well; pa_decode then reports the error.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t split_tokens);
+
+/* Default split length (tokens) used when pa_decode gets split_tokens == 0. */
+int32_t pa_decode_default_split_tokens(void);
+
+/*
+ * pa_decode - paged decode attention, one query row per sequence.
+ *
+ * Defined by [P4] "hand-written Triton kernels" (Decode_Paged_GQAAttention_Kernel:
+ * reads the scattered KV blocks in place through block_table, online softmax, GQA
+ * head mapping inside the kernel) with [P4] "errors, type 1" fixing what
+ * context_lens counts. For sequence s, query head h, g = h / (q_heads/kv_heads),
+ * L = context_lens[s]:
+ *     out[s][h][:] = sum_{j<L} softmax_j(scale * q[s][h] . K_s[j][g]) * V_s[j][g][:]
+ * where K_s[j] is the pool row at slot(s, j). FP8 pools dequantise as code * scale.
+ *
+ *   out          [num_seqs, q_heads, head_dim] of q_dtype, strides (out_stride_tok,
+ *                out_stride_head); every element is written exactly once.
+ *   q            [num_seqs, q_heads, head_dim] of q_dtype, strides (q_stride_tok,
+ *                q_stride_head) (a [B, 1, Hq, D] view works unchanged).
+ *   block_tables [num_seqs, max_blocks_per_seq] int32, row-major. Entries past
+ *                ceil(L / block_size) are never read.
+ *   context_lens [num_seqs] int32, each in [1, max_context_len].
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid).
+ *   scale        softmax scale (e.g. 1/sqrt(head_dim)).
+ *   split_tokens tokens per split-K work item: 0 = pa_decode_default_split_tokens(),
+ *                else a positive multiple of block_size. The split of sequence s
+ *                depends only on context_lens[s] and split_tokens, so a sequence's
+ *                output bits do not depend on the rest of the batch.
+ *   workspace    device scratch of at least pa_decode_workspace_bytes(...) bytes for
+ *                the same (num_seqs, q_heads, head_dim, max_context_len, split_tokens);
+ *                may be NULL when that is 0. Contents on entry are ignored.
+ * Accumulation is fp32; out is rounded once (round-to-nearest-even) to q_dtype.
+ */
+int pa_decode(void *out, int64_t out_stride_tok, int64_t out_stride_head, const void *q,
+              int64_t q_stride_tok, int64_t q_stride_head, int32_t q_dtype, int32_t num_seqs,
+              int32_t q_heads, const pa_kv_pool_t *pool, const int32_t *block_tables,
+              int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+              float scale, int32_t split_tokens, void *workspace, size_t workspace_bytes,
+              void *stream);
+
+/*
+ * pa_varlen_prefill - causal attention for a flat batch of query chunks.
+ *
+ * Defined by [P5] "varlen batch" / "cu_seqlens is only needed in attention" (tokens of
+ * all sequences concatenated, cu_seqlens [num_seqs+1] marks the boundaries, a token
+ * attends only tokens of its own sequence, causally) and [P5]'s per-sequence attention
+ * over the gathered cache with a start position, which a single varlen kernel reading
+ * the paged pool through block_table replaces ("comparison with vLLM").
+ * For sequence s: n_s = cu_seqlens[s+1] - cu_seqlens[s], L_s = context_lens[s] (the
+ * chunk's K/V already stored), P_s = L_s - n_s. Query row i of the chunk (token
+ * cu_seqlens[s] + i) sits at absolute position P_s + i and attends keys 0..P_s+i of
+ * sequence s only:
+ *     out[t][h][:] = sum_{j <= P_s+i} softmax_j(scale * q[t][h] . K_s[j][g]) V_s[j][g][:]
+ *
+ *   q, out       [total_tokens, q_heads, head_dim], strided as in pa_decode.
+ *   cu_seqlens   [num_seqs+1] int32, cu[0] = 0, non-decreasing, cu[num_seqs] =
+ *                total_tokens. n_s == 0 is allowed (no rows).
+ *   max_q_len    host-side upper bound of n_s (sizes the grid).
+ *   Other arguments as in pa_decode. A chunk of length 1 is a decode row.
+ * Supported dtypes: (q BF16, pool BF16) and (q BF16, pool FP8_E4M3). QK^T and PV run
+ * on the matrix cores with bf16 operands (P rounded to bf16) and fp32 accumulation.
+ */
+int pa_varlen_prefill(void *out, int64_t out_stride_tok, int64_t out_stride_head,
+                      const void *q, int64_t q_stride_tok, int64_t q_stride_head,
+                      int32_t q_dtype, const int32_t *cu_seqlens, int32_t num_seqs,
+                      int64_t total_tokens, int32_t max_q_len, int32_t q_heads,
+                      const pa_kv_pool_t *pool, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *context_lens,
+                      int32_t max_context_len, float scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */
