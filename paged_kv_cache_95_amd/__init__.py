@@ -1,0 +1,224 @@
+"""Paged GQA attention over a block-table KV cache for AMD MI355X (gfx950).
+
+Thin Python binding of libpa.so (C ABI declared in include/pa.h). It only marshals
+arguments: checks dtypes, devices and shapes of torch tensors, passes their data
+pointers, element strides and torch's current HIP stream, and raises on a non-zero
+status. Every step of the computation runs in the HIP kernels of the library; there
+is no fallback. PyTorch is used for device memory and streams only.
+
+    pool = KVPool.empty(num_blocks, kv_heads, head_dim, "bf16", device)
+    store_kv(pool, k_new, v_new, slot_mapping)
+    out = decode(q, pool, block_tables, context_lens, scale)
+    out = varlen_prefill(q, cu_seqlens, pool, block_tables, context_lens, scale)
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_OK = 0
+BLOCK_SIZE = 16
+
+_DTYPE_CODE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3}
+_NAME_CODE = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
+_NAME_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+# name -> (restype, argtypes); mirrors include/pa.h
+_P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_decode_default_split_tokens": (_I32, []),
+    "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_store_kv": (ctypes.c_int, [ctypes.POINTER(_Pool), _P, _P, _I32, _I64, _I64, _I64, _I64,
+                                   _I64, _P, _P]),
+    "pa_decode": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32,
+                                 ctypes.POINTER(_Pool), _P, _I32, _P, _I32, _F, _I32, _P, _SZ,
+                                 _P]),
+    "pa_varlen_prefill": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _P, _I32, _I64,
+                                         _I32, _I32, ctypes.POINTER(_Pool), _P, _I32, _P, _I32,
+                                         _F, _P]),
+}
+
+
+def lib():
+    """Load libpa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m paged_kv_cache_95_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_string(status):
+    return lib().pa_status_string(int(status)).decode()
+
+
+def default_split_tokens():
+    return int(lib().pa_decode_default_split_tokens())
+
+
+def _check(status, what):
+    if status != PA_OK:
+        raise PaError(status, what)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+class KVPool:
+    """One layer's paged KV cache: k, v [num_blocks, 16, kv_heads, head_dim] (bf16,
+    fp32, or uint8 e4m3fn codes) and, for FP8, fp32 k_scale/v_scale
+    [num_blocks, 16, kv_heads]. Tensors are owned by the caller (this object)."""
+
+    def __init__(self, k, v, k_scale=None, v_scale=None, dtype=None):
+        _need(k.shape == v.shape and k.dim() == 4, "k/v pools must be 4-D and equal")
+        _need(k.is_contiguous() and v.is_contiguous(), "pools must be dense")
+        self.k, self.v, self.k_scale, self.v_scale = k, v, k_scale, v_scale
+        self.dtype = _DTYPE_CODE[k.dtype] if dtype is None else _NAME_CODE[dtype]
+        if self.dtype == PA_FP8_E4M3:
+            _need(k_scale is not None and v_scale is not None, "FP8 pool needs scales")
+            _need(k_scale.dtype == torch.float32 and k_scale.shape == k.shape[:3]
+                  and k_scale.is_contiguous() and v_scale.is_contiguous()
+                  and v_scale.shape == k.shape[:3], "scales must be fp32 [nb, bs, Hkv]")
+        self.num_blocks, self.block_size, self.kv_heads, self.head_dim = k.shape
+        self._struct = _Pool(k.data_ptr(), v.data_ptr(),
+                             k_scale.data_ptr() if k_scale is not None else 0,
+                             v_scale.data_ptr() if v_scale is not None else 0,
+                             self.num_blocks, self.block_size, self.kv_heads, self.head_dim,
+                             self.dtype)
+
+    @classmethod
+    def empty(cls, num_blocks, kv_heads, head_dim, dtype, device, block_size=BLOCK_SIZE):
+        shape = (num_blocks, block_size, kv_heads, head_dim)
+        td = _NAME_TORCH[dtype]
+        k = torch.empty(shape, dtype=td, device=device)
+        v = torch.empty(shape, dtype=td, device=device)
+        ks = vs = None
+        if dtype == "fp8":
+            ks = torch.empty(shape[:3], dtype=torch.float32, device=device)
+            vs = torch.empty(shape[:3], dtype=torch.float32, device=device)
+        return cls(k, v, ks, vs, dtype=dtype)
+
+    @property
+    def struct(self):
+        return ctypes.byref(self._struct)
+
+
+def _rows3(x, name):
+    """Element strides (token, head) of a [T, H, D] view with unit inner stride."""
+    _need(x.dim() == 3, f"{name} must be [tokens, heads, head_dim]")
+    _need(x.stride(2) == 1, f"{name} needs a unit innermost stride")
+    return x.stride(0), x.stride(1)
+
+
+def store_kv(pool, k, v, slot_mapping):
+    """Write new rows k, v [T, kv_heads, head_dim] (any token/head strides) into the
+    pool at slot_mapping [T] (int64; negative = skip). FP8 pools quantise on store."""
+    ks = _rows3(k, "k")
+    vs = _rows3(v, "v")
+    _need(k.shape == v.shape and k.shape[1:] == (pool.kv_heads, pool.head_dim), "k/v shape")
+    _need(k.dtype == v.dtype, "k/v dtype")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1
+          and slot_mapping.shape[0] == k.shape[0] and slot_mapping.is_contiguous(),
+          "slot_mapping must be contiguous int64 [T]")
+    _check(lib().pa_store_kv(pool.struct, _ptr(k), _ptr(v), _DTYPE_CODE[k.dtype], k.shape[0],
+                             ks[0], ks[1], vs[0], vs[1], _ptr(slot_mapping), _stream()),
+           "pa_store_kv")
+
+
+def decode_workspace_bytes(num_seqs, q_heads, head_dim, max_context_len, split_tokens=0):
+    return int(lib().pa_decode_workspace_bytes(num_seqs, q_heads, head_dim, max_context_len,
+                                               split_tokens))
+
+
+def _meta(block_tables, context_lens):
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.is_contiguous(), "block_tables must be contiguous int32 [B, maxb]")
+    _need(context_lens.dtype == torch.int32 and context_lens.dim() == 1
+          and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
+
+
+def decode(q, pool, block_tables, context_lens, scale, max_context_len=None, split_tokens=0,
+           out=None, workspace=None):
+    """Paged decode: q [B, Hq, D] (strided views allowed) -> out [B, Hq, D].
+    max_context_len: host-side bound of context_lens (default: the block table's
+    capacity; no device sync). workspace: optional preallocated uint8 tensor."""
+    _meta(block_tables, context_lens)
+    B, Hq, D = q.shape
+    if max_context_len is None:
+        max_context_len = block_tables.shape[1] * pool.block_size
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    qs, os_ = _rows3(q, "q"), _rows3(out, "out")
+    need = decode_workspace_bytes(B, Hq, D, max_context_len, split_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_decode(_ptr(out), os_[0], os_[1], _ptr(q), qs[0], qs[1], _DTYPE_CODE[q.dtype],
+                           B, Hq, pool.struct, _ptr(block_tables), block_tables.shape[1],
+                           _ptr(context_lens), int(max_context_len), float(scale),
+                           int(split_tokens), _ptr(workspace), wbytes, _stream()),
+           "pa_decode")
+    return out
+
+
+def varlen_prefill(q, cu_seqlens, pool, block_tables, context_lens, scale, max_q_len=None,
+                   max_context_len=None, out=None):
+    """Varlen causal prefill: q [T, Hq, D] with chunks cu_seqlens [B+1] -> out [T, Hq, D]."""
+    _meta(block_tables, context_lens)
+    _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1
+          and cu_seqlens.is_contiguous(), "cu_seqlens must be contiguous int32 [B+1]")
+    T, Hq, D = q.shape
+    B = cu_seqlens.shape[0] - 1
+    if max_context_len is None:
+        max_context_len = block_tables.shape[1] * pool.block_size
+    if max_q_len is None:
+        max_q_len = min(T, max_context_len)
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=q.dtype, device=q.device)
+    qs, os_ = _rows3(q, "q"), _rows3(out, "out")
+    _check(lib().pa_varlen_prefill(_ptr(out), os_[0], os_[1], _ptr(q), qs[0], qs[1],
+                                   _DTYPE_CODE[q.dtype], _ptr(cu_seqlens), B, T, int(max_q_len),
+                                   Hq, pool.struct, _ptr(block_tables), block_tables.shape[1],
+                                   _ptr(context_lens), int(max_context_len), float(scale),
+                                   _stream()),
+           "pa_varlen_prefill")
+    return out

@@ -1,0 +1,187 @@
+// C ABI of libpa.so: argument validation, workspace sizing and dispatch.
+//
+// Validation runs entirely on the host and before any HIP call, so an invalid call
+// launches nothing (and can be exercised without a GPU). No exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace {
+
+using pa::kBlockSize;
+
+constexpr int kMaxGroup = 8;
+constexpr int kMaxSplitTokens = 1024;  // one wave keeps a split's block ids in its 64 lanes
+
+bool pool_shape_ok(const pa_kv_pool_t* p, int* status) {
+  if (!p || !p->k || !p->v) return *status = PA_ERR_INVALID_ARG, false;
+  if (p->num_blocks <= 0 || p->block_size <= 0 || p->kv_heads <= 0 || p->head_dim <= 0)
+    return *status = PA_ERR_INVALID_ARG, false;
+  if (p->dtype != PA_F32 && p->dtype != PA_BF16 && p->dtype != PA_FP8_E4M3)
+    return *status = PA_ERR_INVALID_ARG, false;
+  if (p->dtype == PA_FP8_E4M3 && (!p->k_scale || !p->v_scale))
+    return *status = PA_ERR_INVALID_ARG, false;
+  if (p->block_size != kBlockSize) return *status = PA_ERR_UNSUPPORTED, false;
+  if (p->head_dim != 64 && p->head_dim != 128) return *status = PA_ERR_UNSUPPORTED, false;
+  return true;
+}
+
+bool q_dtype_ok(int q_dtype, int pool_dtype) {
+  return (q_dtype == PA_F32 && pool_dtype == PA_F32) ||
+         (q_dtype == PA_BF16 && (pool_dtype == PA_BF16 || pool_dtype == PA_FP8_E4M3));
+}
+
+int effective_split(int split_tokens) {
+  return split_tokens == 0 ? pa::kDefaultSplitTokens : split_tokens;
+}
+
+int launched(int status) {
+  if (status != PA_OK) return status;
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape or dtype not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
+    default: return "unknown pa status";
+  }
+}
+
+int32_t pa_decode_default_split_tokens(void) { return pa::kDefaultSplitTokens; }
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t split_tokens) {
+  if (num_seqs <= 0 || q_heads <= 0 || head_dim <= 0 || max_context_len <= 0 ||
+      split_tokens < 0)
+    return 0;
+  const int split = effective_split(split_tokens);
+  const int64_t max_splits = ((int64_t)max_context_len + split - 1) / split;
+  if (max_splits <= 1) return 0;
+  return (size_t)num_seqs * q_heads * max_splits * (head_dim + 1) * sizeof(float);
+}
+
+int pa_store_kv(const pa_kv_pool_t* pool, const void* k, const void* v, int32_t src_dtype,
+                int64_t num_tokens, int64_t k_stride_tok, int64_t k_stride_head,
+                int64_t v_stride_tok, int64_t v_stride_head, const int64_t* slot_mapping,
+                void* stream) {
+  int status = PA_OK;
+  if (!pool_shape_ok(pool, &status)) return status;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  const bool src_ok = pool->dtype == PA_FP8_E4M3
+                          ? (src_dtype == PA_BF16 || src_dtype == PA_F32)
+                          : src_dtype == pool->dtype;
+  if (!src_ok) return PA_ERR_INVALID_ARG;
+  if (k_stride_tok < 0 || k_stride_head < 0 || v_stride_tok < 0 || v_stride_head < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping) return PA_ERR_INVALID_ARG;
+  return launched(pa::launch_store(*pool, k, v, src_dtype, num_tokens, k_stride_tok,
+                                   k_stride_head, v_stride_tok, v_stride_head, slot_mapping,
+                                   (hipStream_t)stream));
+}
+
+int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const void* q,
+              int64_t q_stride_tok, int64_t q_stride_head, int32_t q_dtype, int32_t num_seqs,
+              int32_t q_heads, const pa_kv_pool_t* pool, const int32_t* block_tables,
+              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+              float scale, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  int status = PA_OK;
+  if (!pool_shape_ok(pool, &status)) return status;
+  if (num_seqs < 0 || q_heads <= 0 || q_heads % pool->kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (q_heads / pool->kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (!q_dtype_ok(q_dtype, pool->dtype)) return PA_ERR_INVALID_ARG;
+  if (out_stride_tok < 0 || out_stride_head < 0 || q_stride_tok < 0 || q_stride_head < 0)
+    return PA_ERR_INVALID_ARG;
+  if (split_tokens < 0 || split_tokens % kBlockSize != 0 || split_tokens > kMaxSplitTokens)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq <= 0 || max_context_len <= 0 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlockSize)
+    return PA_ERR_INVALID_ARG;
+  const int split = effective_split(split_tokens);
+  const int max_splits = (max_context_len + split - 1) / split;
+  const size_t need =
+      pa_decode_workspace_bytes(num_seqs, q_heads, pool->head_dim, max_context_len, split);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  const int64_t grid = (int64_t)((max_splits + 3) / 4) * pool->kv_heads * num_seqs;
+  if (grid >= (int64_t)1 << 31 || (int64_t)num_seqs * q_heads >= (int64_t)1 << 31)
+    return PA_ERR_UNSUPPORTED;
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.out_st = out_stride_tok;
+  a.out_sh = out_stride_head;
+  a.q = q;
+  a.q_st = q_stride_tok;
+  a.q_sh = q_stride_head;
+  a.num_seqs = num_seqs;
+  a.q_heads = q_heads;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.split_tokens = split;
+  a.max_splits = max_splits;
+  a.ws_o = (float*)workspace;
+  a.ws_lse = need > 0 ? (float*)workspace + (size_t)num_seqs * q_heads * max_splits * pool->head_dim
+                      : nullptr;
+  return launched(pa::launch_decode(*pool, a, (hipStream_t)stream));
+}
+
+int pa_varlen_prefill(void* out, int64_t out_stride_tok, int64_t out_stride_head,
+                      const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                      int32_t q_dtype, const int32_t* cu_seqlens, int32_t num_seqs,
+                      int64_t total_tokens, int32_t max_q_len, int32_t q_heads,
+                      const pa_kv_pool_t* pool, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, float scale, void* stream) {
+  int status = PA_OK;
+  if (!pool_shape_ok(pool, &status)) return status;
+  if (num_seqs < 0 || total_tokens < 0 || q_heads <= 0 || q_heads % pool->kv_heads != 0)
+    return PA_ERR_INVALID_ARG;
+  if (q_heads / pool->kv_heads > kMaxGroup) return PA_ERR_UNSUPPORTED;
+  if (!q_dtype_ok(q_dtype, pool->dtype)) return PA_ERR_INVALID_ARG;
+  if (pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (out_stride_tok < 0 || out_stride_head < 0 || q_stride_tok < 0 || q_stride_head < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_tokens == 0) return PA_OK;
+  if (!out || !q || !cu_seqlens || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (max_q_len <= 0 || max_blocks_per_seq <= 0 || max_context_len <= 0 ||
+      max_q_len > max_context_len ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlockSize)
+    return PA_ERR_INVALID_ARG;
+  const int64_t tiles = ((int64_t)max_q_len * (q_heads / pool->kv_heads) + 127) / 128;
+  if (tiles * pool->kv_heads * num_seqs >= (int64_t)1 << 31) return PA_ERR_UNSUPPORTED;
+
+  pa::PrefillArgs a;
+  a.out = out;
+  a.out_st = out_stride_tok;
+  a.out_sh = out_stride_head;
+  a.q = q;
+  a.q_st = q_stride_tok;
+  a.q_sh = q_stride_head;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.max_q_len = max_q_len;
+  a.q_heads = q_heads;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  return launched(pa::launch_prefill(*pool, a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Device helpers shared by the paged-attention kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+// ------------------------------------------------------------------ element traits
+// KV element kinds (same numbering as the PA_* dtype enum).
+constexpr int kF32 = PA_F32;
+constexpr int kBF16 = PA_BF16;
+constexpr int kFP8 = PA_FP8_E4M3;
+
+template <int T>
+struct ElemBytes;
+template <>
+struct ElemBytes<kF32> { static constexpr int value = 4; };
+template <>
+struct ElemBytes<kBF16> { static constexpr int value = 2; };
+template <>
+struct ElemBytes<kFP8> { static constexpr int value = 1; };
+
+// ------------------------------------------------------------------ bf16 <-> f32
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------------------ OCP e4m3fn
+// Encode a finite fp32 value to e4m3fn: round to nearest even, saturate to +-448
+// (code 0x7E), keep the sign (so -0 and negative underflow give 0x80).
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __uint_as_float(u & 0x7fffffffu);
+  uint32_t code;
+  if (!(a < 448.0f)) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {
+    // subnormal range: value = m * 2^-9, m = round-half-even(a * 512) in [0, 8]
+    // (m == 8 is the smallest normal, whose code is also 8)
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    // normal range: drop 20 mantissa bits with round-half-even, then rebias the
+    // exponent from 127 to 7 (3 mantissa bits sit right below the exponent)
+    uint32_t ua = u & 0x7fffffffu;
+    ua += 0x7ffffu + ((ua >> 20) & 1u);
+    code = (ua >> 20) - (120u << 3);
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return sign | code;
+}
+
+// Two e4m3fn codes (bytes 0,1 or 2,3 of w) -> two fp32 values (exact).
+__device__ __forceinline__ void e4m3x2_to_f32(uint32_t w, bool high, float& a, float& b) {
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  float2_t r = high ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  a = r[0];
+  b = r[1];
+}
+
+// Pack the bf16 images of two fp32 values that are exactly representable in bf16
+// (low half = lo, high half = hi).
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// ------------------------------------------------------------------ cross-lane
+// DPP controls (within 4-lane quads / 16-lane rows of a wave64).
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+constexpr int kRowRor12 = 0x12C;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace pa

@@ -1,0 +1,55 @@
+// Internal launchers behind the C ABI (arguments already validated by api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+constexpr int kBlockSize = 16;
+constexpr int kDefaultSplitTokens = 256;
+
+int launch_store(const pa_kv_pool_t& pool, const void* k, const void* v, int src_dtype,
+                 int64_t num_tokens, int64_t k_st, int64_t k_sh, int64_t v_st, int64_t v_sh,
+                 const int64_t* slot_mapping, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  int64_t out_st, out_sh;
+  const void* q;
+  int64_t q_st, q_sh;
+  int num_seqs, q_heads;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int max_context_len;
+  float scale;
+  int split_tokens;
+  int max_splits;
+  float* ws_o;    // [num_seqs, q_heads, max_splits, head_dim]
+  float* ws_lse;  // [num_seqs, q_heads, max_splits]
+};
+
+int launch_decode(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  int64_t out_st, out_sh;
+  const void* q;
+  int64_t q_st, q_sh;
+  const int32_t* cu_seqlens;
+  int num_seqs;
+  int64_t total_tokens;
+  int max_q_len, q_heads;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int max_context_len;
+  float scale;
+};
+
+int launch_prefill(const pa_kv_pool_t& pool, const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pa

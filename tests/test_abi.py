@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: libpa.so loads, exports every entry point include/pa.h
+declares, and rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_95_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIB_PATH):
+        pytest.fail("libpa.so not built (python -m paged_kv_cache_95_amd.build)")
+    return pa.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared()
+    assert set(names) >= {"pa_store_kv", "pa_decode", "pa_varlen_prefill",
+                          "pa_decode_workspace_bytes", "pa_status_string",
+                          "pa_decode_default_split_tokens"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in pa.SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings(lib):
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
+        assert pa.status_string(s).startswith("PA_")
+    assert "unknown" in pa.status_string(7)
+
+
+def fake_pool(dtype=pa.PA_BF16, head_dim=128, block_size=16, kv_heads=2, scales=False):
+    # host addresses that are never dereferenced: validation fails or succeeds first
+    p = pa._Pool(0x1000, 0x2000, 0x3000 if scales else 0, 0x4000 if scales else 0,
+                 64, block_size, kv_heads, head_dim, dtype)
+    return p
+
+
+def store(lib, pool, src=pa.PA_BF16, T=0, k=0x5000, v=0x6000, sm=0x7000, st=(256, 128)):
+    return lib.pa_store_kv(ctypes.byref(pool) if pool is not None else None, k, v, src, T,
+                           st[0], st[1], st[0], st[1], sm, None)
+
+
+def test_store_validation(lib):
+    assert store(lib, None) == INVALID
+    assert store(lib, fake_pool()) == OK                          # T == 0: no launch
+    assert store(lib, fake_pool(), T=-1) == INVALID
+    assert store(lib, fake_pool(head_dim=96)) == UNSUPPORTED
+    assert store(lib, fake_pool(block_size=32)) == UNSUPPORTED
+    assert store(lib, fake_pool(dtype=9)) == INVALID
+    assert store(lib, fake_pool(dtype=pa.PA_FP8_E4M3)) == INVALID  # no scales
+    assert store(lib, fake_pool(), src=pa.PA_F32) == INVALID     # dtype mismatch
+    assert store(lib, fake_pool(dtype=pa.PA_FP8_E4M3, scales=True), src=pa.PA_FP8_E4M3) == INVALID
+    assert store(lib, fake_pool(), T=4, k=0) == INVALID
+    assert store(lib, fake_pool(), T=4, sm=0) == INVALID
+    assert store(lib, fake_pool(), T=4, st=(-1, 128)) == INVALID
+    p = fake_pool()
+    p.num_blocks = 0
+    assert store(lib, p) == INVALID
+
+
+def decode(lib, pool, q_dtype=pa.PA_BF16, B=2, Hq=12, maxb=8, maxctx=128, split=0, ws=0,
+           wsb=0, out=0x8000, q=0x9000, bt=0xA000, ctx=0xB000):
+    return lib.pa_decode(out, 1536, 128, q, 1536, 128, q_dtype, B, Hq, ctypes.byref(pool), bt,
+                         maxb, ctx, maxctx, 0.1, split, ws, wsb, None)
+
+
+def test_decode_validation(lib):
+    p = fake_pool()
+    assert decode(lib, p, B=0) == OK
+    assert decode(lib, p, B=-1) == INVALID
+    assert decode(lib, p, Hq=13) == INVALID                 # not a multiple of kv_heads
+    assert decode(lib, p, Hq=18) == UNSUPPORTED              # group of 9
+    assert decode(lib, p, q_dtype=pa.PA_F32) == INVALID      # f32 q on a bf16 pool
+    assert decode(lib, fake_pool(pa.PA_F32), q_dtype=pa.PA_BF16) == INVALID
+    assert decode(lib, p, out=0) == INVALID
+    assert decode(lib, p, bt=0) == INVALID
+    assert decode(lib, p, maxctx=129) == INVALID             # beyond the table's capacity
+    assert decode(lib, p, maxctx=0) == INVALID
+    assert decode(lib, p, split=8) == INVALID                # not a multiple of 16
+    assert decode(lib, p, split=2048) == INVALID             # beyond 1024
+    # 128 tokens at the default split of 256 need no workspace; split 16 needs one
+    assert decode(lib, p, split=16, ws=0) == WORKSPACE
+    need = lib.pa_decode_workspace_bytes(2, 12, 128, 128, 16)
+    assert need == 2 * 12 * 8 * 129 * 4
+    assert decode(lib, p, split=16, ws=0xC000, wsb=need - 1) == WORKSPACE
+
+
+def test_workspace_bytes(lib):
+    d = lib.pa_decode_default_split_tokens()
+    assert d % 16 == 0 and 16 <= d <= 1024
+    assert lib.pa_decode_workspace_bytes(4, 8, 64, d, 0) == 0
+    assert lib.pa_decode_workspace_bytes(4, 8, 64, d + 1, 0) == 4 * 8 * 2 * 65 * 4
+    assert lib.pa_decode_workspace_bytes(0, 8, 64, 100, 0) == 0
+    assert lib.pa_decode_workspace_bytes(4, 8, 64, 100, -16) == 0
+
+
+def prefill(lib, pool, q_dtype=pa.PA_BF16, B=2, T=10, maxq=8, Hq=12, maxb=8, maxctx=128,
+            cu=0xD000):
+    return lib.pa_varlen_prefill(0x8000, 1536, 128, 0x9000, 1536, 128, q_dtype, cu, B, T, maxq,
+                                 Hq, ctypes.byref(pool), 0xA000, maxb, 0xB000, maxctx, 0.1, None)
+
+
+def test_prefill_validation(lib):
+    p = fake_pool()
+    assert prefill(lib, p, B=0) == OK
+    assert prefill(lib, p, T=0) == OK
+    assert prefill(lib, p, T=-1) == INVALID
+    assert prefill(lib, p, cu=0) == INVALID
+    assert prefill(lib, p, maxq=0) == INVALID
+    assert prefill(lib, p, maxq=200) == INVALID              # longer than any context
+    assert prefill(lib, p, Hq=18) == UNSUPPORTED
+    assert prefill(lib, fake_pool(pa.PA_F32), q_dtype=pa.PA_F32) == UNSUPPORTED

@@ -1,0 +1,113 @@
+"""pa_varlen_prefill on the GPU against the fp64 oracle, plus varlen invariants."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_95_amd as pa
+import workloads as W
+from oracle import ref
+
+from _harness import TOL, Setup, max_err
+
+pytestmark = pytest.mark.gpu
+
+
+def check(setup, tol=None):
+    out = setup.gpu()
+    torch.cuda.synchronize()
+    err = max_err(out, setup.oracle())
+    tol = tol or TOL[setup.case.kv_dtype]
+    print(f"{setup.case.name} max_abs_err={err:.3e} tol={tol}", flush=True)
+    assert err <= tol
+    return out
+
+
+def test_varlen_mixed_config(dev):
+    check(Setup(W.make(3), dev, poison=False))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 6, 8])
+def test_random_shapes(dev, D, G):
+    hkv = 2 if G <= 4 else 1
+    case = W.random_case(300 + G * 10 + D, kind="varlen", B=6, Hq=G * hkv, Hkv=hkv, D=D,
+                         lmin=1, lmax=400, nmax=150)
+    check(Setup(case, dev))
+
+
+def test_zero_query_gives_causal_prefix_mean(dev):
+    """q = 0: every visible key weighs the same, so row i of chunk s is the mean of V over
+    keys 0..P_s+i; pins the mask, the start positions and the cu_seqlens boundaries."""
+    case = W.random_case(21, kind="varlen", B=5, Hq=6, Hkv=2, D=128, lmin=1, lmax=300, nmax=90)
+    case.q[:] = 0
+    s = Setup(case, dev)
+    out = s.gpu().float().cpu().numpy()
+    G = 3
+    for b in range(case.num_seqs):
+        a, e = case.cu_seqlens[b], case.cu_seqlens[b + 1]
+        L = int(case.context_lens[b])
+        V = ref.gather_seq(s.ref_v, case.block_tables[b], L)
+        csum = np.cumsum(V, axis=0) / np.arange(1, L + 1)[:, None, None]
+        for i in range(e - a):
+            p = L - (e - a) + i
+            for h in range(6):
+                assert np.max(np.abs(out[a + i, h] - csum[p, h // G])) <= TOL["bf16"]
+
+
+def test_sequences_do_not_attend_across_boundaries(dev):
+    case = W.random_case(22, kind="varlen", B=4, Hq=12, Hkv=2, D=128, lmin=20, lmax=300,
+                         nmax=60)
+    s = Setup(case, dev)
+    out = s.gpu()
+    # perturb sequence 1's queries and every slot of its blocks
+    a, e = int(case.cu_seqlens[1]), int(case.cu_seqlens[2])
+    q2 = s.q.clone()
+    q2[a:e] += 1.0
+    for blk in case.block_tables[1]:
+        if blk >= 0:
+            s.pool.k[int(blk)] += 2.0
+            s.pool.v[int(blk)] -= 3.0
+    out2 = pa.varlen_prefill(q2, s.cu, s.pool, s.bt, s.ctx, case.scale,
+                             max_q_len=case.max_q_len, max_context_len=case.max_context_len)
+    keep = torch.ones(out.shape[0], dtype=torch.bool)
+    keep[a:e] = False
+    assert torch.equal(out[keep.to(dev)], out2[keep.to(dev)])
+
+
+def test_decode_equals_varlen_with_chunks_of_one(dev):
+    case = W.random_case(23, B=8, Hq=12, Hkv=2, D=128, lmin=1, lmax=700)
+    s = Setup(case, dev)
+    dec = s.gpu()
+    cu = torch.arange(case.num_seqs + 1, dtype=torch.int32, device=dev)
+    var = pa.varlen_prefill(s.q, cu, s.pool, s.bt, s.ctx, case.scale, max_q_len=1,
+                            max_context_len=case.max_context_len)
+    assert torch.max(torch.abs(dec.float() - var.float())).item() <= 2 * TOL["bf16"]
+    assert max_err(var, s.oracle()) <= TOL["bf16"]
+
+
+def test_block_permutation_is_bit_identical(dev):
+    case = W.random_case(24, kind="varlen", B=5, Hq=8, Hkv=2, D=128, lmin=5, lmax=500,
+                         nmax=200)
+    s = Setup(case, dev)
+    out = s.gpu()
+    perm = np.random.default_rng(2).permutation(case.num_blocks)
+    inv = np.argsort(perm)
+    bt2 = np.where(case.block_tables >= 0, inv[np.maximum(case.block_tables, 0)], -1)
+    p = torch.from_numpy(perm).to(dev)
+    pool2 = pa.KVPool(s.pool.k[p].contiguous(), s.pool.v[p].contiguous())
+    out2 = pa.varlen_prefill(s.q, s.cu, pool2, torch.from_numpy(bt2.astype(np.int32)).to(dev),
+                             s.ctx, case.scale, max_q_len=case.max_q_len,
+                             max_context_len=case.max_context_len)
+    assert torch.equal(out, out2)
+
+
+def test_empty_chunks_and_strided_q(dev):
+    case = W.random_case(25, kind="varlen", B=6, Hq=6, Hkv=2, D=64, lmin=1, lmax=100, nmax=40)
+    s = Setup(case, dev)
+    T = s.q.shape[0]
+    qb = torch.zeros((T, 7, 64), dtype=torch.bfloat16, device=dev)
+    qb[:, 1:] = s.q
+    out = pa.varlen_prefill(qb[:, 1:], s.cu, s.pool, s.bt, s.ctx, case.scale,
+                            max_q_len=max(1, case.max_q_len),
+                            max_context_len=case.max_context_len)
+    assert max_err(out, s.oracle()) <= TOL["bf16"]

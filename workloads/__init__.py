@@ -299,6 +299,23 @@ def host_pool(case, which, poison_unused=None):
     return x
 
 
+def prefix_tokens(case):
+    """Context tokens that are not stored in this step, as (seq, pos) arrays, plus a
+    bf16 source row for each (K and V, [n, Hkv, D] float32 values). Used to populate
+    FP8 pools through the store, so both the GPU and the oracle quantise them."""
+    new = set(zip(case.new_seq.tolist(), case.new_pos.tolist()))
+    rows = [(s, p) for s in range(case.num_seqs) for p in range(int(case.context_lens[s]))
+            if (s, p) not in new]
+    seqs = np.array([r[0] for r in rows], dtype=np.int64)
+    pos = np.array([r[1] for r in rows], dtype=np.int64)
+    rng = np.random.default_rng([case.seed, 7])
+    k = normal(rng, (len(rows), case.Hkv, case.D), "bf16")
+    v = normal(rng, (len(rows), case.Hkv, case.D), "bf16")
+    slots = _slots(case.block_tables, seqs, pos, case.block_size) if len(rows) else \
+        np.zeros(0, np.int64)
+    return seqs, pos, slots, k, v
+
+
 def fill_device_normal_(tensor, seed):
     """Fill a torch tensor (any float dtype, on its device) with N(0,1) from a seeded
     generator on that device; values are rounded to the tensor's dtype by torch."""
