@@ -136,8 +136,11 @@ int pa_store_kv(const pa_kv_pool_t *pool, const void *k, const void *v, int32_t 
 
 /*
  * pa_decode_workspace_bytes - bytes of device workspace pa_decode needs for these
- * sizes and this split length (0 when no context can need more than one split).
- * Returns 0 for invalid arguments as well; pa_decode then reports the error.
+ * sizes and this split length (0 when no context can need more than one split):
+ * num_seqs*q_heads int32 counters rounded up to 256 bytes, then
+ * num_seqs*q_heads*max_splits*(head_dim+1) fp32 partials, with
+ * max_splits = ceil(max_context_len / split). Returns 0 for invalid arguments as
+ * well; pa_decode then reports the error.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t split_tokens);
@@ -171,7 +174,12 @@ int32_t pa_decode_default_split_tokens(void);
  *                output bits do not depend on the rest of the batch.
  *   workspace    device scratch of at least pa_decode_workspace_bytes(...) bytes for
  *                the same (num_seqs, q_heads, head_dim, max_context_len, split_tokens);
- *                may be NULL when that is 0. Contents on entry are ignored.
+ *                may be NULL when that is 0. It must be ZERO-FILLED before its first
+ *                use: its leading words are per-(sequence, KV head) arrival counters
+ *                that the last split of each group uses to merge the partials, and
+ *                every call leaves them zero again when its kernel completes. The
+ *                rest holds per-split partials (lse, o) and is overwritten each call.
+ *                Two calls in flight must not share a workspace.
  * Accumulation is fp32; out is rounded once (round-to-nearest-even) to q_dtype.
  */
 int pa_decode(void *out, int64_t out_stride_tok, int64_t out_stride_head, const void *q,

@@ -169,6 +169,13 @@ def decode_workspace_bytes(num_seqs, q_heads, head_dim, max_context_len, split_t
                                                split_tokens))
 
 
+def decode_workspace(num_seqs, q_heads, head_dim, max_context_len, split_tokens=0,
+                     device="cuda"):
+    """A zero-filled workspace for decode() calls of at most these sizes."""
+    need = decode_workspace_bytes(num_seqs, q_heads, head_dim, max_context_len, split_tokens)
+    return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
+
+
 def _meta(block_tables, context_lens):
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
           and block_tables.is_contiguous(), "block_tables must be contiguous int32 [B, maxb]")
@@ -180,7 +187,8 @@ def decode(q, pool, block_tables, context_lens, scale, max_context_len=None, spl
            out=None, workspace=None):
     """Paged decode: q [B, Hq, D] (strided views allowed) -> out [B, Hq, D].
     max_context_len: host-side bound of context_lens (default: the block table's
-    capacity; no device sync). workspace: optional preallocated uint8 tensor."""
+    capacity; no device sync). workspace: optional preallocated uint8 tensor, zero-filled
+    before its first use (decode_workspace()); reusing one keeps the call allocation-free."""
     _meta(block_tables, context_lens)
     B, Hq, D = q.shape
     if max_context_len is None:
@@ -190,7 +198,8 @@ def decode(q, pool, block_tables, context_lens, scale, max_context_len=None, spl
     qs, os_ = _rows3(q, "q"), _rows3(out, "out")
     need = decode_workspace_bytes(B, Hq, D, max_context_len, split_tokens)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled once: its leading words are arrival counters the kernel resets
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pa_decode(_ptr(out), os_[0], os_[1], _ptr(q), qs[0], qs[1], _DTYPE_CODE[q.dtype],
                            B, Hq, pool.struct, _ptr(block_tables), block_tables.shape[1],

@@ -56,6 +56,14 @@ const char* pa_status_string(int status) {
 }
 
 int32_t pa_decode_default_split_tokens(void) { return pa::kDefaultSplitTokens; }
+}  // extern "C"
+
+size_t pa::decode_counter_bytes(int num_seqs, int q_heads) {
+  const size_t b = (size_t)num_seqs * q_heads * sizeof(int);
+  return (b + 255) / 256 * 256;
+}
+
+extern "C" {
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t split_tokens) {
@@ -65,7 +73,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t head
   const int split = effective_split(split_tokens);
   const int64_t max_splits = ((int64_t)max_context_len + split - 1) / split;
   if (max_splits <= 1) return 0;
-  return (size_t)num_seqs * q_heads * max_splits * (head_dim + 1) * sizeof(float);
+  return pa::decode_counter_bytes(num_seqs, q_heads) +
+         (size_t)num_seqs * q_heads * max_splits * (head_dim + 1) * sizeof(float);
 }
 
 int pa_store_kv(const pa_kv_pool_t* pool, const void* k, const void* v, int32_t src_dtype,
@@ -133,9 +142,15 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
   a.scale = scale;
   a.split_tokens = split;
   a.max_splits = max_splits;
-  a.ws_o = (float*)workspace;
-  a.ws_lse = need > 0 ? (float*)workspace + (size_t)num_seqs * q_heads * max_splits * pool->head_dim
-                      : nullptr;
+  if (need > 0) {
+    char* w = (char*)workspace;
+    a.counters = (int*)w;
+    a.ws_o = (float*)(w + pa::decode_counter_bytes(num_seqs, q_heads));
+    a.ws_lse = a.ws_o + (size_t)num_seqs * q_heads * max_splits * pool->head_dim;
+  } else {
+    a.counters = nullptr;
+    a.ws_o = a.ws_lse = nullptr;
+  }
   return launched(pa::launch_decode(*pool, a, (hipStream_t)stream));
 }
 

@@ -5,7 +5,9 @@
 // through block_table, online softmax, GQA mapping inside the kernel). Splitting a
 // long context into fixed-length pieces whose (lse, o) partials are merged by
 // log-sum-exp is not on the pages; it is how one wave's worth of work is kept small
-// enough to fill 256 CUs.
+// enough to fill 256 CUs. The merge runs in the same launch: each split writes its
+// normalised partial and log2-sum-exp, then counts its arrival on a per-(sequence,
+// KV head) counter; the last arrival merges the group and resets the counter.
 //
 // Work item = (sequence s, KV head g, split i) = one wavefront, which serves all G
 // query heads of the group, so every K/V byte is read once. Per 16-token block:
@@ -205,7 +207,8 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(
     const void* __restrict__ q, int64_t q_st, int64_t q_sh, int num_seqs, int splits_per_row,
     const int32_t* __restrict__ block_tables, int max_blocks_per_seq,
     const int32_t* __restrict__ context_lens, int max_context_len, float scale_log2,
-    int split_tokens, int max_splits, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    int split_tokens, int max_splits, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    int* __restrict__ counters) {
   using Gm = Geom<KVT, D>;
   constexpr float NEG_INF = -__builtin_huge_valf();
   const int lane = threadIdx.x & 63;
@@ -342,23 +345,26 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(
     inv_l[h] = 1.0f / lr;
     lse2[h] = M + __log2f(lr);
   }
-  if (lane >= 16) return;
   const int d0 = cv * Gm::EV;
   if (nsplit == 1) {
+    if (lane < 16) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int64_t o = (int64_t)s * out_st + (int64_t)(g * G + h) * out_sh + d0;
-      if constexpr (QT == kF32) {
+      for (int h = 0; h < G; ++h) {
+        const int64_t o = (int64_t)s * out_st + (int64_t)(g * G + h) * out_sh + d0;
+        if constexpr (QT == kF32) {
 #pragma unroll
-        for (int e = 0; e < Gm::EV; ++e) ((float*)out)[o + e] = st.acc[h][e] * inv_l[h];
-      } else {
+          for (int e = 0; e < Gm::EV; ++e) ((float*)out)[o + e] = st.acc[h][e] * inv_l[h];
+        } else {
 #pragma unroll
-        for (int e = 0; e < Gm::EV; ++e)
-          ((uint16_t*)out)[o + e] = f32_to_bf16(st.acc[h][e] * inv_l[h]);
+          for (int e = 0; e < Gm::EV; ++e)
+            ((uint16_t*)out)[o + e] = f32_to_bf16(st.acc[h][e] * inv_l[h]);
+        }
       }
     }
-  } else {
-    const int hq = hkv * G;
+    return;
+  }
+  const int hq = hkv * G;
+  if (lane < 16) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const int64_t row = ((int64_t)s * hq + g * G + h) * max_splits + split;
@@ -368,42 +374,53 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(
       if (cv == 0) ws_lse[row] = lse2[h];
     }
   }
-}
-
-// One wavefront per (sequence, query head) with more than one split.
-template <int D, int QT>
-__global__ void __launch_bounds__(64) decode_merge_kernel(
-    void* __restrict__ out, int64_t out_st, int64_t out_sh, int q_heads,
-    const int32_t* __restrict__ context_lens, int max_context_len, int split_tokens,
-    int max_splits, const float* __restrict__ ws_o, const float* __restrict__ ws_lse) {
-  const int h = blockIdx.x % q_heads;
-  const int s = blockIdx.x / q_heads;
-  const int L = min(context_lens[s], max_context_len);
-  const int nsplit = L > 0 ? (L + split_tokens - 1) / split_tokens : 0;
-  if (nsplit <= 1) return;
-  const int64_t row0 = ((int64_t)s * q_heads + h) * max_splits;
-  float M = -__builtin_huge_valf();
-  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ws_lse[row0 + i]);
+  // ---- the last split of (s, g) to finish merges the group's partials:
+  // out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M), M = max_i lse_i.
+  // Release our partials, count, and let only the last arrival read them back.
+  __threadfence();
+  int* counter = counters + (int64_t)s * hkv + g;
+  int old = 0;
+  if (lane == 0) old = atomicAdd(counter, 1);
+  old = __shfl(old, 0);
+  if (old != nsplit - 1) return;
+  __threadfence();
   constexpr int PER = D / 64;
-  float acc[PER];
+#pragma unroll 1
+  for (int h = 0; h < G; ++h) {
+    const int64_t row0 = ((int64_t)s * hq + g * G + h) * max_splits;
+    // lse values are read with per-lane addresses (vector loads through the coherent
+    // path), then broadcast with readlane
+    float M = NEG_INF;
+    for (int i0 = 0; i0 < nsplit; i0 += 64)
+      if (i0 + lane < nsplit) M = fmaxf(M, ws_lse[row0 + i0 + lane]);
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  float den = 0.0f;
-  for (int i = 0; i < nsplit; ++i) {
-    const float w = fast_exp2(ws_lse[row0 + i] - M);
-    den += w;
-    const float* o = ws_o + (row0 + i) * D;
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float acc[PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[threadIdx.x + 64 * e], acc[e]);
+    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+    float den = 0.0f;
+    for (int i0 = 0; i0 < nsplit; i0 += 64) {
+      const float w_lane = i0 + lane < nsplit ? fast_exp2(ws_lse[row0 + i0 + lane] - M) : 0.0f;
+      const int cnt = min(64, nsplit - i0);
+      for (int i = 0; i < cnt; ++i) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), i));
+        den += w;
+        const float* o = ws_o + (row0 + i0 + i) * D;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[lane + 64 * e], acc[e]);
+      }
+    }
+    const float inv = 1.0f / den;
+    const int64_t base = (int64_t)s * out_st + (int64_t)(g * G + h) * out_sh;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int d = lane + 64 * e;
+      if constexpr (QT == kF32) ((float*)out)[base + d] = acc[e] * inv;
+      else ((uint16_t*)out)[base + d] = f32_to_bf16(acc[e] * inv);
+    }
   }
-  const float inv = 1.0f / den;
-  const int64_t base = (int64_t)s * out_st + (int64_t)h * out_sh;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int d = threadIdx.x + 64 * e;
-    if constexpr (QT == kF32) ((float*)out)[base + d] = acc[e] * inv;
-    else ((uint16_t*)out)[base + d] = f32_to_bf16(acc[e] * inv);
-  }
+  // every split of this group has arrived: leave the counter at zero for the next call
+  if (lane == 0) *counter = 0;
 }
 
 template <int KVT, int D, int G, int QT>
@@ -414,11 +431,8 @@ static void launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, hipSt
       (const char*)pool.k, (const char*)pool.v, pool.k_scale, pool.v_scale, pool.num_blocks,
       pool.kv_heads, a.out, a.out_st, a.out_sh, a.q, a.q_st, a.q_sh, a.num_seqs,
       splits_per_row, a.block_tables, a.max_blocks_per_seq, a.context_lens,
-      a.max_context_len, a.scale * kLog2e, a.split_tokens, a.max_splits, a.ws_o, a.ws_lse);
-  if (a.max_splits > 1)
-    decode_merge_kernel<D, QT><<<(unsigned)((int64_t)a.num_seqs * a.q_heads), 64, 0, stream>>>(
-        a.out, a.out_st, a.out_sh, a.q_heads, a.context_lens, a.max_context_len,
-        a.split_tokens, a.max_splits, a.ws_o, a.ws_lse);
+      a.max_context_len, a.scale * kLog2e, a.split_tokens, a.max_splits, a.ws_o, a.ws_lse,
+      a.counters);
 }
 
 template <int KVT, int D, int QT>

@@ -28,9 +28,14 @@ struct DecodeArgs {
   float scale;
   int split_tokens;
   int max_splits;
+  int* counters;  // [num_seqs * kv_heads] arrival counters, zero between calls
   float* ws_o;    // [num_seqs, q_heads, max_splits, head_dim]
   float* ws_lse;  // [num_seqs, q_heads, max_splits]
 };
+
+// Workspace layout of pa_decode: counters (num_seqs * q_heads ints, 256-byte aligned
+// size), then the partial outputs, then the partial log-sum-exps.
+size_t decode_counter_bytes(int num_seqs, int q_heads);
 
 int launch_decode(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream);
 

@@ -96,7 +96,7 @@ def test_decode_validation(lib):
     # 128 tokens at the default split of 256 need no workspace; split 16 needs one
     assert decode(lib, p, split=16, ws=0) == WORKSPACE
     need = lib.pa_decode_workspace_bytes(2, 12, 128, 128, 16)
-    assert need == 2 * 12 * 8 * 129 * 4
+    assert need == 256 + 2 * 12 * 8 * 129 * 4        # counters (rounded) + partials
     assert decode(lib, p, split=16, ws=0xC000, wsb=need - 1) == WORKSPACE
 
 
@@ -104,7 +104,8 @@ def test_workspace_bytes(lib):
     d = lib.pa_decode_default_split_tokens()
     assert d % 16 == 0 and 16 <= d <= 1024
     assert lib.pa_decode_workspace_bytes(4, 8, 64, d, 0) == 0
-    assert lib.pa_decode_workspace_bytes(4, 8, 64, d + 1, 0) == 4 * 8 * 2 * 65 * 4
+    assert lib.pa_decode_workspace_bytes(4, 8, 64, d + 1, 0) == 256 + 4 * 8 * 2 * 65 * 4
+    assert lib.pa_decode_workspace_bytes(40, 8, 64, d + 1, 0) == 1280 + 40 * 8 * 2 * 65 * 4
     assert lib.pa_decode_workspace_bytes(0, 8, 64, 100, 0) == 0
     assert lib.pa_decode_workspace_bytes(4, 8, 64, 100, -16) == 0
 

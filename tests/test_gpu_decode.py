@@ -241,3 +241,47 @@ def test_fp8_decode_sampled_and_permuted_twin(dev):
         worst = max(worst, float(np.max(np.abs(out[b:b + 1] - exp))))
     print(f"fp8_decode sampled max_abs_err={worst:.3e}", flush=True)
     assert worst <= TOL["fp8"]
+
+
+def test_workspace_reuse_leaves_counters_zero(dev):
+    """The fused merge counts split arrivals in the workspace; every call must leave the
+    counters at zero so the next call (other contexts, other split) merges correctly."""
+    ws = pa.decode_workspace(8, 12, 128, 3000, 16, device=dev)
+    for seed, split in ((51, 16), (52, 32), (53, 16), (54, 64), (55, 16)):
+        case = W.random_case(seed, B=8, Hq=12, Hkv=2, D=128, lmin=1, lmax=3000)
+        s = Setup(case, dev)
+        out = pa.decode(s.q, s.pool, s.bt, s.ctx, case.scale, max_context_len=3000,
+                        split_tokens=split, workspace=ws)
+        torch.cuda.synchronize()
+        assert max_err(out, s.oracle()) <= TOL["bf16"]
+        assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+
+
+def test_graph_replay_matches_eager(dev):
+    """Store + decode captured in a HIP graph: every replay, with eager work and
+    synchronisations in between, reproduces the eager result bit for bit."""
+    case = W.random_case(56, B=6, Hq=12, Hkv=2, D=128, lmin=100, lmax=2500)
+    s = Setup(case, dev)
+    ws = pa.decode_workspace(6, 12, 128, 2500, 64, device=dev)
+    out = torch.empty_like(s.q)
+
+    def step():
+        pa.store_kv(s.pool, s.k_new, s.v_new, s.slots)
+        pa.decode(s.q, s.pool, s.bt, s.ctx, case.scale, max_context_len=2500, split_tokens=64,
+                  out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert max_err(eager, s.oracle()) <= TOL["bf16"]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        out.zero_()
+        junk = torch.randn(1000, device=dev).sum()      # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        del junk
