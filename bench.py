@@ -109,7 +109,7 @@ def qwen_layers(torch, pa, W, dev, split_tokens):
                                    50000 + l)
         out = torch.empty((B, hq, D), dtype=torch.bfloat16, device=dev)
         layers.append((pool, q, kn, vn, out))
-    ws = pa.decode_workspace(B, hq, D, maxctx, split_tokens, device=dev)
+    ws = pa.decode_workspace(B, hq, hkv, D, maxctx, split_tokens, device=dev)
 
     def store_all():
         for pool, q, kn, vn, out in layers:
@@ -162,7 +162,7 @@ def cpu_baseline(case, budget_s=12.0):
                       f"(affinity {len(os.sched_getaffinity(0))})"}
 
 
-def extra_large_decode(torch, pa, W, dev, reps=20):
+def extra_large_decode(torch, pa, W, dev, reps=20, split_tokens=0):
     case = W.make(4)
     pool = pa.KVPool.empty(case.num_blocks, case.Hkv, case.D, "bf16", dev)
     W.fill_device_normal_(pool.k, 41)
@@ -175,9 +175,10 @@ def extra_large_decode(torch, pa, W, dev, reps=20):
     slots = torch.from_numpy(case.slot_mapping).to(dev)
     out = torch.empty_like(q)
     maxctx = case.max_context_len
-    ws = pa.decode_workspace(case.num_seqs, case.Hq, case.D, maxctx, 0, device=dev)
+    ws = pa.decode_workspace(case.num_seqs, case.Hq, case.Hkv, case.D, maxctx, split_tokens,
+                             device=dev)
     g = capture(torch, lambda: pa.decode(q, pool, bt, ctx, case.scale, max_context_len=maxctx,
-                                         out=out, workspace=ws))
+                                         split_tokens=split_tokens, out=out, workspace=ws))
     gs = capture(torch, lambda: pa.store_kv(pool, kn, vn, slots))
     for _ in range(3):
         g.replay()
@@ -193,7 +194,7 @@ def extra_large_decode(torch, pa, W, dev, reps=20):
             "seqs_per_s": round(case.num_seqs / ((ms + ms_store) / 1e3), 1)}
 
 
-def extra_fp8_decode(torch, pa, W, dev, reps=30, copies=2):
+def extra_fp8_decode(torch, pa, W, dev, reps=30, copies=2, split_tokens=0):
     """Two copies of the 64 x 8192 FP8 multi-slot pool (277 MB each) alternate, so a call
     does not find its pool in the MALL left by the previous one."""
     case = W.make(5)
@@ -219,11 +220,12 @@ def extra_fp8_decode(torch, pa, W, dev, reps=30, copies=2):
     vn = torch.from_numpy(case.v_new).to(torch.bfloat16).to(dev)
     slots = torch.from_numpy(case.slot_mapping).to(dev)
     out = torch.empty_like(q)
-    ws = pa.decode_workspace(B, case.Hq, D, ctx_len, 0, device=dev)
+    ws = pa.decode_workspace(B, case.Hq, hkv, D, ctx_len, split_tokens, device=dev)
 
     def dec():
         for p in pools:
-            pa.decode(q, p, bt, ctx, case.scale, max_context_len=ctx_len, out=out, workspace=ws)
+            pa.decode(q, p, bt, ctx, case.scale, max_context_len=ctx_len,
+                      split_tokens=split_tokens, out=out, workspace=ws)
 
     def sto():
         for p in pools:
@@ -335,7 +337,7 @@ def main():
                    "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": D, "block_size": 16,
                    "pool_blocks": case.num_blocks, "layers": LAYERS,
                    "context_lens": case.context_lens.tolist(),
-                   "split_tokens": args.split_tokens or pa.default_split_tokens(),
+                   "split_tokens": args.split_tokens or pa.default_split_tokens(B, hkv, 3200),
                    "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(B / (ms_step / 1e3), 1),

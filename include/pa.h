@@ -137,16 +137,20 @@ int pa_store_kv(const pa_kv_pool_t *pool, const void *k, const void *v, int32_t 
 /*
  * pa_decode_workspace_bytes - bytes of device workspace pa_decode needs for these
  * sizes and this split length (0 when no context can need more than one split):
- * num_seqs*q_heads int32 counters rounded up to 256 bytes, then
  * num_seqs*q_heads*max_splits*(head_dim+1) fp32 partials, with
  * max_splits = ceil(max_context_len / split). Returns 0 for invalid arguments as
  * well; pa_decode then reports the error.
  */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t split_tokens);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t split_tokens);
 
-/* Default split length (tokens) used when pa_decode gets split_tokens == 0. */
-int32_t pa_decode_default_split_tokens(void);
+/* Split length (tokens) pa_decode uses for split_tokens == 0 with this call shape: the
+ * power of two in [32, 512] nearest above num_seqs*kv_heads*max_context_len/2048, so
+ * that a worst-case batch has about 2048 (sequence, KV head, split) work items. Returns
+ * 0 for non-positive arguments. */
+int32_t pa_decode_default_split_tokens(int32_t num_seqs, int32_t kv_heads,
+                                       int32_t max_context_len);
 
 /*
  * pa_decode - paged decode attention, one query row per sequence.
@@ -168,18 +172,18 @@ int32_t pa_decode_default_split_tokens(void);
  *   context_lens [num_seqs] int32, each in [1, max_context_len].
  *   max_context_len  host-side upper bound of context_lens (sizes the grid).
  *   scale        softmax scale (e.g. 1/sqrt(head_dim)).
- *   split_tokens tokens per split-K work item: 0 = pa_decode_default_split_tokens(),
- *                else a positive multiple of block_size. The split of sequence s
- *                depends only on context_lens[s] and split_tokens, so a sequence's
- *                output bits do not depend on the rest of the batch.
+ *   split_tokens tokens per split-K work item: a positive multiple of block_size, at
+ *                most 1024, or 0 for pa_decode_default_split_tokens(num_seqs,
+ *                kv_heads, max_context_len). With a given split length the split of
+ *                sequence s depends only on context_lens[s], so its output bits do
+ *                not depend on the rest of the batch; pass an explicit value to keep
+ *                that when batch shapes vary.
  *   workspace    device scratch of at least pa_decode_workspace_bytes(...) bytes for
- *                the same (num_seqs, q_heads, head_dim, max_context_len, split_tokens);
- *                may be NULL when that is 0. It must be ZERO-FILLED before its first
- *                use: its leading words are per-(sequence, KV head) arrival counters
- *                that the last split of each group uses to merge the partials, and
- *                every call leaves them zero again when its kernel completes. The
- *                rest holds per-split partials (lse, o) and is overwritten each call.
- *                Two calls in flight must not share a workspace.
+ *                the same (num_seqs, q_heads, kv_heads, head_dim, max_context_len,
+ *                split_tokens);
+ *                may be NULL when that is 0. It holds the per-split partials (o, lse),
+ *                is fully overwritten before it is read, so its contents on entry are
+ *                ignored. Two calls in flight must not share a workspace.
  * Accumulation is fp32; out is rounded once (round-to-nearest-even) to q_dtype.
  */
 int pa_decode(void *out, int64_t out_stride_tok, int64_t out_stride_head, const void *q,

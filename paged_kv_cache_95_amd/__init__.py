@@ -48,8 +48,8 @@ _lib = None
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-    "pa_decode_default_split_tokens": (_I32, []),
-    "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_decode_default_split_tokens": (_I32, [_I32, _I32, _I32]),
+    "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_store_kv": (ctypes.c_int, [ctypes.POINTER(_Pool), _P, _P, _I32, _I64, _I64, _I64, _I64,
                                    _I64, _P, _P]),
     "pa_decode": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32,
@@ -81,8 +81,9 @@ def status_string(status):
     return lib().pa_status_string(int(status)).decode()
 
 
-def default_split_tokens():
-    return int(lib().pa_decode_default_split_tokens())
+def default_split_tokens(num_seqs, kv_heads, max_context_len):
+    """Split length decode() uses for split_tokens=0 at this call shape."""
+    return int(lib().pa_decode_default_split_tokens(num_seqs, kv_heads, max_context_len))
 
 
 def _check(status, what):
@@ -164,16 +165,18 @@ def store_kv(pool, k, v, slot_mapping):
            "pa_store_kv")
 
 
-def decode_workspace_bytes(num_seqs, q_heads, head_dim, max_context_len, split_tokens=0):
-    return int(lib().pa_decode_workspace_bytes(num_seqs, q_heads, head_dim, max_context_len,
-                                               split_tokens))
+def decode_workspace_bytes(num_seqs, q_heads, kv_heads, head_dim, max_context_len,
+                           split_tokens=0):
+    return int(lib().pa_decode_workspace_bytes(num_seqs, q_heads, kv_heads, head_dim,
+                                               max_context_len, split_tokens))
 
 
-def decode_workspace(num_seqs, q_heads, head_dim, max_context_len, split_tokens=0,
+def decode_workspace(num_seqs, q_heads, kv_heads, head_dim, max_context_len, split_tokens=0,
                      device="cuda"):
-    """A zero-filled workspace for decode() calls of at most these sizes."""
-    need = decode_workspace_bytes(num_seqs, q_heads, head_dim, max_context_len, split_tokens)
-    return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
+    """A workspace for decode() calls of these sizes (and split length)."""
+    need = decode_workspace_bytes(num_seqs, q_heads, kv_heads, head_dim, max_context_len,
+                                  split_tokens)
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
 
 
 def _meta(block_tables, context_lens):
@@ -196,10 +199,9 @@ def decode(q, pool, block_tables, context_lens, scale, max_context_len=None, spl
     if out is None:
         out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
     qs, os_ = _rows3(q, "q"), _rows3(out, "out")
-    need = decode_workspace_bytes(B, Hq, D, max_context_len, split_tokens)
+    need = decode_workspace_bytes(B, Hq, pool.kv_heads, D, max_context_len, split_tokens)
     if need and workspace is None:
-        # zero-filled once: its leading words are arrival counters the kernel resets
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pa_decode(_ptr(out), os_[0], os_[1], _ptr(q), qs[0], qs[1], _DTYPE_CODE[q.dtype],
                            B, Hq, pool.struct, _ptr(block_tables), block_tables.shape[1],

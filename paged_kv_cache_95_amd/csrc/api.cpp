@@ -31,8 +31,17 @@ bool q_dtype_ok(int q_dtype, int pool_dtype) {
          (q_dtype == PA_BF16 && (pool_dtype == PA_BF16 || pool_dtype == PA_FP8_E4M3));
 }
 
-int effective_split(int split_tokens) {
-  return split_tokens == 0 ? pa::kDefaultSplitTokens : split_tokens;
+// Split length used when the caller passes 0: aim at about 2048 (sequence, KV head,
+// split) work items for the worst case of every context at max_context_len (eight
+// waves per CU), as a power of two in [32, 512] tokens. Small batches get short splits
+// (more waves in flight for a latency-bound call), large ones long splits (fewer
+// partials to merge).
+int effective_split(int split_tokens, int64_t num_seqs, int kv_heads, int max_context_len) {
+  if (split_tokens != 0) return split_tokens;
+  const int64_t want = num_seqs * kv_heads * (int64_t)max_context_len / 2048;
+  int split = 32;
+  while (split < 512 && split < want) split <<= 1;
+  return split;
 }
 
 int launched(int status) {
@@ -55,26 +64,22 @@ const char* pa_status_string(int status) {
   }
 }
 
-int32_t pa_decode_default_split_tokens(void) { return pa::kDefaultSplitTokens; }
-}  // extern "C"
-
-size_t pa::decode_counter_bytes(int num_seqs, int q_heads) {
-  const size_t b = (size_t)num_seqs * q_heads * sizeof(int);
-  return (b + 255) / 256 * 256;
+int32_t pa_decode_default_split_tokens(int32_t num_seqs, int32_t kv_heads,
+                                       int32_t max_context_len) {
+  if (num_seqs <= 0 || kv_heads <= 0 || max_context_len <= 0) return 0;
+  return effective_split(0, num_seqs, kv_heads, max_context_len);
 }
 
-extern "C" {
-
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t split_tokens) {
-  if (num_seqs <= 0 || q_heads <= 0 || head_dim <= 0 || max_context_len <= 0 ||
-      split_tokens < 0)
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t split_tokens) {
+  if (num_seqs <= 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len <= 0 || split_tokens < 0)
     return 0;
-  const int split = effective_split(split_tokens);
+  const int split = effective_split(split_tokens, num_seqs, kv_heads, max_context_len);
   const int64_t max_splits = ((int64_t)max_context_len + split - 1) / split;
   if (max_splits <= 1) return 0;
-  return pa::decode_counter_bytes(num_seqs, q_heads) +
-         (size_t)num_seqs * q_heads * max_splits * (head_dim + 1) * sizeof(float);
+  return (size_t)num_seqs * q_heads * max_splits * (head_dim + 1) * sizeof(float);
 }
 
 int pa_store_kv(const pa_kv_pool_t* pool, const void* k, const void* v, int32_t src_dtype,
@@ -117,12 +122,12 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
   if (max_blocks_per_seq <= 0 || max_context_len <= 0 ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlockSize)
     return PA_ERR_INVALID_ARG;
-  const int split = effective_split(split_tokens);
+  const int split = effective_split(split_tokens, num_seqs, pool->kv_heads, max_context_len);
   const int max_splits = (max_context_len + split - 1) / split;
-  const size_t need =
-      pa_decode_workspace_bytes(num_seqs, q_heads, pool->head_dim, max_context_len, split);
+  const size_t need = pa_decode_workspace_bytes(num_seqs, q_heads, pool->kv_heads,
+                                                pool->head_dim, max_context_len, split);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-  const int64_t grid = (int64_t)((max_splits + 3) / 4) * pool->kv_heads * num_seqs;
+  const int64_t grid = ((int64_t)num_seqs * max_splits * pool->kv_heads + 3) / 4;
   if (grid >= (int64_t)1 << 31 || (int64_t)num_seqs * q_heads >= (int64_t)1 << 31)
     return PA_ERR_UNSUPPORTED;
 
@@ -142,15 +147,9 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
   a.scale = scale;
   a.split_tokens = split;
   a.max_splits = max_splits;
-  if (need > 0) {
-    char* w = (char*)workspace;
-    a.counters = (int*)w;
-    a.ws_o = (float*)(w + pa::decode_counter_bytes(num_seqs, q_heads));
-    a.ws_lse = a.ws_o + (size_t)num_seqs * q_heads * max_splits * pool->head_dim;
-  } else {
-    a.counters = nullptr;
-    a.ws_o = a.ws_lse = nullptr;
-  }
+  a.ws_o = (float*)workspace;  // [num_seqs, q_heads, max_splits, head_dim], then lse
+  a.ws_lse = need > 0 ? a.ws_o + (size_t)num_seqs * q_heads * max_splits * pool->head_dim
+                      : nullptr;
   return launched(pa::launch_decode(*pool, a, (hipStream_t)stream));
 }
 

@@ -5,47 +5,52 @@
 // through block_table, online softmax, GQA mapping inside the kernel). Splitting a
 // long context into fixed-length pieces whose (lse, o) partials are merged by
 // log-sum-exp is not on the pages; it is how one wave's worth of work is kept small
-// enough to fill 256 CUs. The merge runs in the same launch: each split writes its
-// normalised partial and log2-sum-exp, then counts its arrival on a per-(sequence,
-// KV head) counter; the last arrival merges the group and resets the counter.
+// enough to fill 256 CUs. Each split writes its normalised partial and log2-sum-exp to
+// the workspace; a second, small launch merges them.
 //
-// Work item = (sequence s, KV head g, split i) = one wavefront, which serves all G
-// query heads of the group, so every K/V byte is read once. Per 16-token block:
+// Work item = (sequence s, split i, KV head g) = one wavefront, which serves all G
+// query heads of the group, so every K/V byte is read once; the KV heads of one split
+// are neighbouring work items, so a pool block (all KV heads of 16 tokens) is fetched
+// by one workgroup at about the same time. Lane = 16r + 8h + t (DPP row r, half h):
 //
-//   K side  lane = 16r + 4t + c holds token 4t + r of the block; c selects the
-//           16-byte chunks c, c+4, ... of that token's row. Partial dots over those
-//           chunks, a quad butterfly (DPP) finishes q.k for all G heads.
-//   softmax each 16-lane DPP row r owns tokens {r, r+4, r+8, r+12} and keeps its own
-//           running max / sum per head, so the per-block max is a 2-step row rotate;
-//           the four rows are combined once per split, like split partials.
-//   V side  lane = 16r + cv accumulates head dims [cv*D/16, (cv+1)*D/16) for the
-//           row's four tokens; the probabilities reach it by row rotations of 4, 8
-//           and 12 lanes, and the token each rotation delivers is found by rotating
-//           the token index the same way.
+//   K side  the 8 lanes of a half-row share one token and each loads 16-byte chunks
+//           t, t+8, ... of its row, so one load instruction covers whole 128-byte lines
+//           of 8 tokens. Partial dots over those chunks, then quad and half-row
+//           butterflies (DPP) give q.k for all G heads. Token of (set k, row r, half h)
+//           = 8k + 2r + h, so row r owns tokens {2r, 2r+1, 8+2r, 9+2r}.
+//   softmax each DPP row keeps its own running max / sum per head: the block max is a
+//           local max over the two sets plus one row mirror; the four rows are
+//           combined once per split, like split partials.
+//   V side  lane 16r + c accumulates head dims [c*D/16, (c+1)*D/16) over the row's
+//           four tokens, each read as a full row (16 lanes); the probabilities of the
+//           other half-row's tokens arrive by a row mirror.
 //
-// Loads are 16-byte per lane and each instruction covers whole 64-byte pieces of 16
-// token rows (K) or four full rows (V); the next block is loaded while the current one
-// is computed. Tokens past the context (the tail of the last block) are excluded by
-// selects, never by multiplying with zero, so stale or NaN slots cannot leak in.
+// A ring of block buffers keeps the next blocks' loads in flight while the current one
+// is computed; KV loads are non-temporal (read once per call). Tokens past the context
+// (the tail of the last block) are excluded by selects, never by multiplying with
+// zero, so stale or NaN slots cannot leak in.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
 namespace pa {
 
 constexpr int kWaves = 4;  // wavefronts (independent work items) per 256-thread block
+constexpr int kRowMirror = 0x140;
+constexpr int kHalfMirror = 0x141;
 
 template <int KVT, int D>
 struct Geom {
   static constexpr int E = ElemBytes<KVT>::value;
-  static constexpr int ROW = D * E;      // bytes of one token row of one KV head
-  static constexpr int NCH = ROW / 16;   // 16-byte chunks per row
-  static constexpr int KCH = NCH / 4;    // chunks per K-lane
-  static constexpr int EPC = 16 / E;     // elements per chunk
-  static constexpr int EK = KCH * EPC;   // elements per K-lane (D / 4)
-  static constexpr int EV = D / 16;      // elements per V-lane
-  static constexpr int VB = EV * E;      // bytes per V-lane per token
-  static constexpr int VW = VB / 4;      // dwords per V-lane per token
-  static constexpr int QW = KVT == kF32 ? EK : EK / 2;  // query registers per head
+  static constexpr int ROW = D * E;                   // bytes of one token row, one KV head
+  static constexpr int NCH = ROW / 16;                // 16-byte chunks per row
+  static constexpr int KC = NCH >= 8 ? NCH / 8 : 1;   // chunks per K-lane per token
+  static constexpr int EPC = 16 / E;                  // elements per chunk
+  static constexpr int QW = KVT == kF32 ? 4 * KC : (KVT == kBF16 ? 4 * KC : 8 * KC);
+  static constexpr int EV = D / 16;                   // elements per V-lane per token
+  static constexpr int VB = EV * E;                   // bytes per V-lane per token
+  static constexpr int VW = VB / 4;                   // dwords per V-lane per token
 };
 
 template <int N>
@@ -53,25 +58,32 @@ __device__ __forceinline__ void load_dwords(const char* p, uint32_t (&w)[N]) {
   if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < N / 4; ++i) {
-      const uint4 x = reinterpret_cast<const uint4*>(p)[i];
+      const uint4 x = ld_stream16(p + 16 * i);
       w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
     }
   } else if constexpr (N == 2) {
-    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    const uint2 x = ld_stream8(p);
     w[0] = x.x; w[1] = x.y;
   } else {
     static_assert(N == 1, "unsupported V width");
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
+    w[0] = ld_stream4(p);
   }
 }
 
 template <int KVT, int D>
 struct BlockBuf {
   using Gm = Geom<KVT, D>;
-  uint32_t k[Gm::KCH * 4];
-  uint32_t v[4][Gm::VW];
-  float ks, vs;
+  uint32_t k[2][Gm::KC * 4];  // [token set][dwords]
+  uint32_t v[4][Gm::VW];      // [row token][dwords]
+  float ks[2], vs[2];         // FP8 scales of the K-lane tokens
   int nvalid;
+};
+
+// Blocks kept in flight per wave: three where the registers allow it without losing a
+// wave per SIMD, else two.
+template <int KVT, int G>
+struct RingDepth {
+  static constexpr int value = G <= 4 ? 3 : 2;
 };
 
 template <int KVT, int D, int G>
@@ -79,221 +91,277 @@ struct DecodeState {
   using Gm = Geom<KVT, D>;
   float acc[G][Gm::EV];
   float m[G];  // running max of this lane's DPP row (log2 domain)
-  float l[G];  // running sum of this lane's own token's weights
+  float l[G];  // running sum of this lane's DPP row
 };
 
 template <int KVT, int D, int G, bool MASKED>
 __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeState<KVT, D, G>& st,
                                               const uint32_t (&qw)[G][Geom<KVT, D>::QW],
-                                              float scale_log2, int tok_k, const int (&tok_v)[4]) {
+                                              float scale_log2, const int (&tok_k)[2],
+                                              const int (&tok_v)[4]) {
   using Gm = Geom<KVT, D>;
   constexpr float NEG_INF = -__builtin_huge_valf();
-  // ---- scores: partial dot over this lane's chunks, then the quad butterfly
-  float s[G];
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  // ---- scores of the two K tokens of this lane
+  float s[2][G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) s[h] = 0.0f;
-  if constexpr (KVT == kBF16) {
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  for (int k = 0; k < 2; ++k) {
 #pragma unroll
-    for (int w = 0; w < Gm::KCH * 4; ++w)
+    for (int h = 0; h < G; ++h) s[k][h] = 0.0f;
+    if constexpr (KVT == kBF16) {
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-        s[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][w]),
-                                               __builtin_bit_cast(bf2, b.k[w]), s[h], false);
-  } else if constexpr (KVT == kFP8) {
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+      for (int w = 0; w < Gm::KC * 4; ++w)
 #pragma unroll
-    for (int w = 0; w < Gm::KCH * 4; ++w) {
-      float x0, x1, x2, x3;
-      e4m3x2_to_f32(b.k[w], false, x0, x1);
-      e4m3x2_to_f32(b.k[w], true, x2, x3);
-      const uint32_t p0 = pack_bf16_exact(x0, x1), p1 = pack_bf16_exact(x2, x3);
+        for (int h = 0; h < G; ++h)
+          s[k][h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][w]),
+                                                    __builtin_bit_cast(bf2, b.k[k][w]), s[k][h],
+                                                    false);
+    } else if constexpr (KVT == kFP8) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        s[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][2 * w]),
-                                               __builtin_bit_cast(bf2, p0), s[h], false);
-        s[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][2 * w + 1]),
-                                               __builtin_bit_cast(bf2, p1), s[h], false);
+      for (int w = 0; w < Gm::KC * 4; ++w) {
+        float x0, x1, x2, x3;
+        e4m3x2_to_f32(b.k[k][w], false, x0, x1);
+        e4m3x2_to_f32(b.k[k][w], true, x2, x3);
+        const uint32_t p0 = pack_bf16_exact(x0, x1), p1 = pack_bf16_exact(x2, x3);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          s[k][h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][2 * w]),
+                                                    __builtin_bit_cast(bf2, p0), s[k][h], false);
+          s[k][h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][2 * w + 1]),
+                                                    __builtin_bit_cast(bf2, p1), s[k][h], false);
+        }
       }
+    } else {
+#pragma unroll
+      for (int w = 0; w < Gm::KC * 4; ++w)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          s[k][h] = fmaf(__uint_as_float(qw[h][w]), __uint_as_float(b.k[k][w]), s[k][h]);
     }
-  } else {
-#pragma unroll
-    for (int w = 0; w < Gm::KCH * 4; ++w)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        s[h] = fmaf(__uint_as_float(qw[h][w]), __uint_as_float(b.k[w]), s[h]);
   }
-  const float sc = KVT == kFP8 ? scale_log2 * b.ks : scale_log2;
-  const bool valid_k = !MASKED || tok_k < b.nvalid;
-  float p[G];
-  bool rescale = false;
+  bool valid_k[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) valid_k[k] = !MASKED || tok_k[k] < b.nvalid;
+  float p_own[2][G], p_oth[2][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float x = s[h];
-    x += dpp<kQuadXor1>(x);
-    x += dpp<kQuadXor2>(x);
-    x *= sc;
-    if (MASKED) x = valid_k ? x : NEG_INF;
-    float mb = fmaxf(x, dpp<kRowRor4>(x));
-    mb = fmaxf(mb, dpp<kRowRor8>(mb));
+    float x[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float y = s[k][h];
+      y += dpp<kQuadXor1>(y);
+      y += dpp<kQuadXor2>(y);
+      y += dpp<kHalfMirror>(y);
+      y *= KVT == kFP8 ? scale_log2 * b.ks[k] : scale_log2;
+      x[k] = MASKED ? (valid_k[k] ? y : NEG_INF) : y;
+    }
+    float mb = fmaxf(x[0], x[1]);
+    mb = fmaxf(mb, dpp<kRowMirror>(mb));  // max over the row's four tokens
     const float m_new = fmaxf(st.m[h], mb);
-    float alpha, ph;
+    float alpha;
     if (MASKED) {
       // a row may have seen no valid token yet (m_new = -inf): keep it at zero
       alpha = m_new == NEG_INF ? 1.0f : fast_exp2(st.m[h] - m_new);
-      ph = valid_k ? fast_exp2(x - m_new) : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) p_own[k][h] = valid_k[k] ? fast_exp2(x[k] - m_new) : 0.0f;
     } else {
       alpha = fast_exp2(st.m[h] - m_new);
-      ph = fast_exp2(x - m_new);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) p_own[k][h] = fast_exp2(x[k] - m_new);
     }
-    rescale |= alpha != 1.0f;
-    st.l[h] = fmaf(st.l[h], alpha, ph);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) p_oth[k][h] = dpp<kRowMirror>(p_own[k][h]);
+    st.l[h] = fmaf(st.l[h], alpha, (p_own[0][h] + p_oth[0][h]) + (p_own[1][h] + p_oth[1][h]));
     st.m[h] = m_new;
-    p[h] = ph;
-    if (__any(rescale)) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
       // alpha is uniform over the DPP row, and the V-lanes of row r own row r's acc
 #pragma unroll
       for (int e = 0; e < Gm::EV; ++e) st.acc[h][e] *= alpha;
     }
-    rescale = false;
   }
   if constexpr (KVT == kFP8) {
+    // fold the V scale of each token into its probability (the mirror delivers the
+    // other half-row's already scaled values); invalid tokens stay exactly 0
 #pragma unroll
-    for (int h = 0; h < G; ++h) p[h] = valid_k ? p[h] * b.vs : 0.0f;
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        p_own[k][h] = valid_k[k] ? p_own[k][h] * b.vs[k] : 0.0f;
+        p_oth[k][h] = dpp<kRowMirror>(p_own[k][h]);
+      }
   }
-  // ---- V: four tokens of this row, delivered by row rotations
+  // ---- V: the row's four tokens (own set 0, other set 0, own set 1, other set 1)
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    float pk[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (kk == 0) pk[h] = p[h];
-      else if (kk == 1) pk[h] = dpp<kRowRor4>(p[h]);
-      else if (kk == 2) pk[h] = dpp<kRowRor8>(p[h]);
-      else pk[h] = dpp<kRowRor12>(p[h]);
-    }
-    const bool valid_v = !MASKED || tok_v[kk] < b.nvalid;
+  for (int x = 0; x < 4; ++x) {
+    const bool valid_v = !MASKED || tok_v[x] < b.nvalid;
     float vf[Gm::EV];
     if constexpr (KVT == kBF16) {
 #pragma unroll
       for (int w = 0; w < Gm::VW; ++w) {
-        const uint32_t x = valid_v ? b.v[kk][w] : 0u;
-        vf[2 * w] = bf16_lo(x);
-        vf[2 * w + 1] = bf16_hi(x);
+        const uint32_t y = valid_v ? b.v[x][w] : 0u;
+        vf[2 * w] = bf16_lo(y);
+        vf[2 * w + 1] = bf16_hi(y);
       }
     } else if constexpr (KVT == kFP8) {
 #pragma unroll
       for (int w = 0; w < Gm::VW; ++w) {
-        const uint32_t x = valid_v ? b.v[kk][w] : 0u;
-        e4m3x2_to_f32(x, false, vf[4 * w], vf[4 * w + 1]);
-        e4m3x2_to_f32(x, true, vf[4 * w + 2], vf[4 * w + 3]);
+        const uint32_t y = valid_v ? b.v[x][w] : 0u;
+        e4m3x2_to_f32(y, false, vf[4 * w], vf[4 * w + 1]);
+        e4m3x2_to_f32(y, true, vf[4 * w + 2], vf[4 * w + 3]);
       }
     } else {
 #pragma unroll
-      for (int w = 0; w < Gm::VW; ++w) vf[w] = __uint_as_float(valid_v ? b.v[kk][w] : 0u);
+      for (int w = 0; w < Gm::VW; ++w) vf[w] = __uint_as_float(valid_v ? b.v[x][w] : 0u);
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      const float pk = (x & 1) ? p_oth[x >> 1][h] : p_own[x >> 1][h];
 #pragma unroll
-      for (int e = 0; e < Gm::EV; ++e) st.acc[h][e] = fmaf(pk[h], vf[e], st.acc[h][e]);
+      for (int e = 0; e < Gm::EV; ++e) st.acc[h][e] = fmaf(pk, vf[e], st.acc[h][e]);
+    }
   }
 }
 
+struct SplitArgs {
+  const char* kpool;
+  const char* vpool;
+  const float* kscale;
+  const float* vscale;
+  int64_t num_blocks;
+  int hkv;
+  void* out;
+  int64_t out_st, out_sh;
+  const void* q;
+  int64_t q_st, q_sh;
+  int num_seqs;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int max_context_len;
+  float scale_log2;
+  int split_tokens;
+  int max_splits;
+  float* ws_o;
+  float* ws_lse;
+  bool q_aligned;    // q rows start on 16-byte boundaries (base and strides)
+  bool out_aligned;  // same for out
+};
+
+// Context length as the kernels use it: clamped to the host bound, so a longer value
+// (a contract violation) cannot index past the sequence's workspace rows or its
+// block-table row; its output is then unspecified.
+__device__ __forceinline__ int clamped_len(const SplitArgs& a, int s) {
+  return min(a.context_lens[s], a.max_context_len);
+}
+__device__ __forceinline__ int num_splits(int L, int split_tokens) {
+  return L > 0 ? (L + split_tokens - 1) / split_tokens : 0;
+}
+
+// One work item (sequence s, split, kv head g) on one wavefront.
 template <int KVT, int D, int G, int QT>
-__global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(
-    const char* __restrict__ kpool, const char* __restrict__ vpool,
-    const float* __restrict__ kscale, const float* __restrict__ vscale, int64_t num_blocks,
-    int hkv, void* __restrict__ out, int64_t out_st, int64_t out_sh,
-    const void* __restrict__ q, int64_t q_st, int64_t q_sh, int num_seqs, int splits_per_row,
-    const int32_t* __restrict__ block_tables, int max_blocks_per_seq,
-    const int32_t* __restrict__ context_lens, int max_context_len, float scale_log2,
-    int split_tokens, int max_splits, float* __restrict__ ws_o, float* __restrict__ ws_lse,
-    int* __restrict__ counters) {
+__device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split, int g, int L,
+                                            int nsplit, int lane) {
   using Gm = Geom<KVT, D>;
   constexpr float NEG_INF = -__builtin_huge_valf();
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  // blockIdx.x -> (split group, kv head, sequence), split group fastest
-  const int sg = blockIdx.x % splits_per_row;
-  const int rest = blockIdx.x / splits_per_row;
-  const int g = rest % hkv;
-  const int s = rest / hkv;
-  const int split = sg * kWaves + wave;
-  // a context longer than the host bound would index past this sequence's workspace
-  // rows and block-table row: clamp (contract violation, output then unspecified)
-  const int L = min(context_lens[s], max_context_len);
-  const int nsplit = L > 0 ? (L + split_tokens - 1) / split_tokens : 0;
-  if (split >= nsplit) return;
-  const int t0 = split * split_tokens;
-  const int t1 = min(L, t0 + split_tokens);
+  const int t0 = split * a.split_tokens;
+  const int t1 = min(L, t0 + a.split_tokens);
   const int jb0 = t0 / kBlockSize;
   const int nblk = (t1 - t0 + kBlockSize - 1) / kBlockSize;
 
+  // ---- block ids of this split: lane j holds entry jb0 + j (a split is <= 64 blocks)
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int bid_lane = lane < nblk ? bt_row[jb0 + lane] : 0;
+
   // ---- lane geometry
   const int r = lane >> 4;
-  const int tq = (lane >> 2) & 3;
-  const int c = lane & 3;
+  const int half = (lane >> 3) & 1;
+  const int t8 = lane & 7;
   const int cv = lane & 15;
-  const int tok_k = 4 * tq + r;
-  int tok_v[4];
-  tok_v[0] = tok_k;
-  tok_v[1] = dpp_i<kRowRor4>(tok_k);
-  tok_v[2] = dpp_i<kRowRor8>(tok_k);
-  tok_v[3] = dpp_i<kRowRor12>(tok_k);
+  const bool k_lane = t8 < Gm::NCH;  // false only for rows shorter than 8 chunks
+  int tok_k[2], tok_v[4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    tok_k[k] = 8 * k + 2 * r + half;
+    tok_v[2 * k] = tok_k[k];
+    tok_v[2 * k + 1] = 8 * k + 2 * r + (half ^ 1);
+  }
 
-  // ---- query registers for the G heads of this group
+  // ---- query chunks t8 + 8j of the G heads (bf16 pairs, or fp32)
   uint32_t qw[G][Gm::QW];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const int64_t qoff = (int64_t)s * q_st + (int64_t)(g * G + h) * q_sh;
+    const int64_t qoff = (int64_t)s * a.q_st + (int64_t)(g * G + h) * a.q_sh;
 #pragma unroll
-    for (int i = 0; i < Gm::KCH; ++i) {
-      const int d0 = (c + 4 * i) * Gm::EPC;
+    for (int j = 0; j < Gm::KC; ++j) {
+      const int d0 = (t8 + 8 * j) * Gm::EPC;
+      if (a.q_aligned) {
+        // rows start on 16 bytes: one or two 16-byte loads per chunk
+        constexpr int QE = QT == kF32 ? 4 : 2;
+        constexpr int N16 = Gm::EPC * QE / 16;
+        const char* qp = (const char*)a.q + (qoff + d0) * QE;
+#pragma unroll
+        for (int v = 0; v < N16; ++v) {
+          const uint4 x = k_lane ? *reinterpret_cast<const uint4*>(qp + 16 * v) : make_uint4(0, 0, 0, 0);
+          qw[h][(N16 * j + v) * 4] = x.x;
+          qw[h][(N16 * j + v) * 4 + 1] = x.y;
+          qw[h][(N16 * j + v) * 4 + 2] = x.z;
+          qw[h][(N16 * j + v) * 4 + 3] = x.w;
+        }
+        continue;
+      }
       if constexpr (QT == kF32) {
-        const float* qp = (const float*)q + qoff + d0;
+        const float* qp = (const float*)a.q + qoff + d0;
 #pragma unroll
-        for (int e = 0; e < Gm::EPC; ++e) qw[h][i * Gm::EPC + e] = __float_as_uint(qp[e]);
+        for (int e = 0; e < 4; ++e) qw[h][4 * j + e] = k_lane ? __float_as_uint(qp[e]) : 0u;
       } else {
-        const uint16_t* qp = (const uint16_t*)q + qoff + d0;
+        const uint16_t* qp = (const uint16_t*)a.q + qoff + d0;
+        constexpr int PAIRS = Gm::EPC / 2;
 #pragma unroll
-        for (int e = 0; e < Gm::EPC / 2; ++e)
-          qw[h][i * Gm::EPC / 2 + e] = (uint32_t)qp[2 * e] | ((uint32_t)qp[2 * e + 1] << 16);
+        for (int e = 0; e < PAIRS; ++e)
+          qw[h][PAIRS * j + e] =
+              k_lane ? ((uint32_t)qp[2 * e] | ((uint32_t)qp[2 * e + 1] << 16)) : 0u;
       }
     }
   }
 
-  // ---- block ids of this split: lane j holds entry jb0 + j (split <= 64 blocks)
-  const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
-  const int bid_lane = lane < nblk ? bt_row[jb0 + lane] : 0;
-
-  const int64_t blk_bytes = (int64_t)kBlockSize * hkv * Gm::ROW;
-  const uint32_t kofs = (uint32_t)((tok_k * hkv + g) * Gm::ROW + c * 16);
-  uint32_t vofs[4];
+  const int64_t blk_bytes = (int64_t)kBlockSize * a.hkv * Gm::ROW;
+  uint32_t kofs[2], vofs[4], sofs[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) vofs[kk] = (uint32_t)((tok_v[kk] * hkv + g) * Gm::ROW + cv * Gm::VB);
-  const uint32_t sofs = (uint32_t)(tok_k * hkv + g);
+  for (int k = 0; k < 2; ++k) {
+    kofs[k] = (uint32_t)((tok_k[k] * a.hkv + g) * Gm::ROW + t8 * 16);
+    sofs[k] = (uint32_t)(tok_k[k] * a.hkv + g);
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) vofs[x] = (uint32_t)((tok_v[x] * a.hkv + g) * Gm::ROW + cv * Gm::VB);
 
   auto load = [&](BlockBuf<KVT, D>& b, int j) {
     const int bid_raw = __builtin_amdgcn_readlane(bid_lane, j);
-    const bool ok = (unsigned)bid_raw < (uint64_t)num_blocks;
+    const bool ok = (unsigned)bid_raw < (uint64_t)a.num_blocks;
     const int64_t bid = ok ? bid_raw : 0;
     const int first = (jb0 + j) * kBlockSize;
     b.nvalid = ok ? min(kBlockSize, L - first) : 0;
-    const char* kb = kpool + bid * blk_bytes + kofs;
+    const char* kb = a.kpool + bid * blk_bytes;
 #pragma unroll
-    for (int i = 0; i < Gm::KCH; ++i) {
-      const uint4 x = *reinterpret_cast<const uint4*>(kb + i * 64);
-      b.k[4 * i] = x.x; b.k[4 * i + 1] = x.y; b.k[4 * i + 2] = x.z; b.k[4 * i + 3] = x.w;
-    }
-    const char* vb = vpool + bid * blk_bytes;
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) load_dwords<Gm::VW>(vb + vofs[kk], b.v[kk]);
+      for (int c = 0; c < Gm::KC; ++c) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (k_lane) x = ld_stream16(kb + kofs[k] + c * 128);
+        b.k[k][4 * c] = x.x; b.k[k][4 * c + 1] = x.y; b.k[k][4 * c + 2] = x.z;
+        b.k[k][4 * c + 3] = x.w;
+      }
+    const char* vb = a.vpool + bid * blk_bytes;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) load_dwords<Gm::VW>(vb + vofs[x], b.v[x]);
     if constexpr (KVT == kFP8) {
-      const int64_t sb = bid * kBlockSize * hkv + sofs;
-      b.ks = kscale[sb];
-      b.vs = vscale[sb];
+      const int64_t sb = bid * kBlockSize * a.hkv;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        b.ks[k] = a.kscale[sb + sofs[k]];
+        b.vs[k] = a.vscale[sb + sofs[k]];
+      }
     } else {
-      b.ks = b.vs = 1.0f;
+      b.ks[0] = b.ks[1] = b.vs[0] = b.vs[1] = 1.0f;
     }
   };
 
@@ -307,32 +375,35 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(
   }
   auto process = [&](const BlockBuf<KVT, D>& b) {
     if (b.nvalid == kBlockSize)
-      process_block<KVT, D, G, false>(b, st, qw, scale_log2, tok_k, tok_v);
+      process_block<KVT, D, G, false>(b, st, qw, a.scale_log2, tok_k, tok_v);
     else
-      process_block<KVT, D, G, true>(b, st, qw, scale_log2, tok_k, tok_v);
+      process_block<KVT, D, G, true>(b, st, qw, a.scale_log2, tok_k, tok_v);
   };
 
-  BlockBuf<KVT, D> A, B;
-  load(A, 0);
-  int j = 0;
-  for (; j + 1 < nblk; j += 2) {
-    load(B, j + 1);
-    process(A);
-    if (j + 2 < nblk) load(A, j + 2);
-    process(B);
+  // ring of NB block buffers: block j + NB - 1 is requested before block j is used
+  constexpr int NB = RingDepth<KVT, G>::value;
+  BlockBuf<KVT, D> ring[NB];
+#pragma unroll
+  for (int p = 0; p < NB - 1; ++p)
+    if (p < nblk) load(ring[p], p);
+  for (int j0 = 0; j0 < nblk; j0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int j = j0 + u;
+      if (j >= nblk) break;
+      if (j + NB - 1 < nblk) load(ring[(u + NB - 1) % NB], j + NB - 1);
+      process(ring[u]);
+    }
   }
-  if (j < nblk) process(A);
 
   // ---- combine the four DPP rows: per head, rescale to the wave max and sum
   float inv_l[G], lse2[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float lr = st.l[h] + dpp<kRowRor4>(st.l[h]);
-    lr += dpp<kRowRor8>(lr);  // sum over the row's four tokens
     float M = fmaxf(st.m[h], __shfl_xor(st.m[h], 16));
     M = fmaxf(M, __shfl_xor(M, 32));
     const float f = st.m[h] == NEG_INF ? 0.0f : fast_exp2(st.m[h] - M);
-    lr *= f;
+    float lr = st.l[h] * f;
     lr += __shfl_xor(lr, 16);
     lr += __shfl_xor(lr, 32);
 #pragma unroll
@@ -345,94 +416,286 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(
     inv_l[h] = 1.0f / lr;
     lse2[h] = M + __log2f(lr);
   }
+  if (lane >= 16) return;
   const int d0 = cv * Gm::EV;
   if (nsplit == 1) {
-    if (lane < 16) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const int64_t o = (int64_t)s * out_st + (int64_t)(g * G + h) * out_sh + d0;
-        if constexpr (QT == kF32) {
+    for (int h = 0; h < G; ++h) {
+      const int64_t o = (int64_t)s * a.out_st + (int64_t)(g * G + h) * a.out_sh + d0;
+      if constexpr (QT == kF32) {
 #pragma unroll
-          for (int e = 0; e < Gm::EV; ++e) ((float*)out)[o + e] = st.acc[h][e] * inv_l[h];
+        for (int e = 0; e < Gm::EV; ++e) ((float*)a.out)[o + e] = st.acc[h][e] * inv_l[h];
+      } else {
+        uint32_t w[Gm::EV / 2];
+#pragma unroll
+        for (int e = 0; e < Gm::EV / 2; ++e)
+          w[e] = (uint32_t)f32_to_bf16(st.acc[h][2 * e] * inv_l[h]) |
+                 ((uint32_t)f32_to_bf16(st.acc[h][2 * e + 1] * inv_l[h]) << 16);
+        uint16_t* op = (uint16_t*)a.out + o;
+        if (a.out_aligned && Gm::EV == 8) {
+          *reinterpret_cast<uint4*>(op) = make_uint4(w[0], w[1], w[2], w[3]);
         } else {
 #pragma unroll
-          for (int e = 0; e < Gm::EV; ++e)
-            ((uint16_t*)out)[o + e] = f32_to_bf16(st.acc[h][e] * inv_l[h]);
+          for (int e = 0; e < Gm::EV / 2; ++e) {
+            op[2 * e] = (uint16_t)w[e];
+            op[2 * e + 1] = (uint16_t)(w[e] >> 16);
+          }
         }
       }
     }
     return;
   }
-  const int hq = hkv * G;
-  if (lane < 16) {
+  const int hq = a.hkv * G;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int64_t row = ((int64_t)s * hq + g * G + h) * max_splits + split;
-      float* wo = ws_o + row * D + d0;
-#pragma unroll
-      for (int e = 0; e < Gm::EV; ++e) wo[e] = st.acc[h][e] * inv_l[h];
-      if (cv == 0) ws_lse[row] = lse2[h];
-    }
-  }
-  // ---- the last split of (s, g) to finish merges the group's partials:
-  // out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M), M = max_i lse_i.
-  // Release our partials, count, and let only the last arrival read them back.
-  __threadfence();
-  int* counter = counters + (int64_t)s * hkv + g;
-  int old = 0;
-  if (lane == 0) old = atomicAdd(counter, 1);
-  old = __shfl(old, 0);
-  if (old != nsplit - 1) return;
-  __threadfence();
-  constexpr int PER = D / 64;
-#pragma unroll 1
   for (int h = 0; h < G; ++h) {
-    const int64_t row0 = ((int64_t)s * hq + g * G + h) * max_splits;
-    // lse values are read with per-lane addresses (vector loads through the coherent
-    // path), then broadcast with readlane
-    float M = NEG_INF;
-    for (int i0 = 0; i0 < nsplit; i0 += 64)
-      if (i0 + lane < nsplit) M = fmaxf(M, ws_lse[row0 + i0 + lane]);
+    const int64_t row = ((int64_t)s * hq + g * G + h) * a.max_splits + split;
+    float* wo = a.ws_o + row * D + d0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float acc[PER];
+    for (int e = 0; e < Gm::EV; ++e) wo[e] = st.acc[h][e] * inv_l[h];
+    if (cv == 0) a.ws_lse[row] = lse2[h];
+  }
+}
+
+// One work item per wavefront over the full (sequence, max_splits, kv head) range, kv
+// head fastest; items past a sequence's split count exit at once. Used when the batch
+// is too large for the compact schedule below.
+template <int KVT, int D, int G, int QT>
+__global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(SplitArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int g = (int)(item % a.hkv);
+  const int64_t rest = item / a.hkv;
+  const int split = (int)(rest % a.max_splits);
+  const int s = (int)(rest / a.max_splits);
+  if (s >= a.num_seqs) return;
+  const int L = clamped_len(a, s);
+  const int nsplit = num_splits(L, a.split_tokens);
+  if (split >= nsplit) return;
+  decode_item<KVT, D, G, QT>(a, s, split, g, L, nsplit, lane);
+}
+
+// Compact persistent schedule. Every workgroup prefix-sums the per-sequence split
+// counts into LDS, which enumerates exactly the existing (sequence, split, kv head)
+// items (kv head fastest, four per workgroup step); workgroup b then walks the b-th
+// contiguous share of them. Dispatching only real work matters for skewed batches:
+// padding the grid to max_context_len would launch mostly empty workgroups.
+constexpr int kMaxCompactSeqs = 4096;
+
+__device__ __forceinline__ int block_exclusive_scan(int x, int* wave_sums, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-    float den = 0.0f;
-    for (int i0 = 0; i0 < nsplit; i0 += 64) {
-      const float w_lane = i0 + lane < nsplit ? fast_exp2(ws_lse[row0 + i0 + lane] - M) : 0.0f;
-      const int cnt = min(64, nsplit - i0);
-      for (int i = 0; i < cnt; ++i) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), i));
-        den += w;
-        const float* o = ws_o + (row0 + i0 + i) * D;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wave_sums[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[lane + 64 * e], acc[e]);
+  for (int w = 0; w < kWaves; ++w) {
+    const int v = wave_sums[w];
+    before += w < wave ? v : 0;
+    total += v;
+  }
+  __syncthreads();
+  return before + incl - x;
+}
+
+template <int KVT, int D, int G, int QT>
+__global__ void __launch_bounds__(64 * kWaves) decode_compact_kernel(SplitArgs a) {
+  __shared__ int cum[kMaxCompactSeqs + 1];  // cum[s] = splits of sequences before s
+  __shared__ int wave_sums[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int carry = 0;
+  for (int base = 0; base < a.num_seqs; base += 64 * kWaves) {
+    const int s = base + (int)threadIdx.x;
+    const int n = s < a.num_seqs ? num_splits(clamped_len(a, s), a.split_tokens) : 0;
+    int tot;
+    const int ex = block_exclusive_scan(n, wave_sums, tot);
+    if (s < a.num_seqs) cum[s] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) cum[a.num_seqs] = carry;
+  __syncthreads();
+  const int64_t entries = (int64_t)carry * a.hkv;
+  const int64_t steps = (entries + kWaves - 1) / kWaves;
+  const int64_t first = (int64_t)blockIdx.x * steps / gridDim.x;
+  const int64_t last = ((int64_t)blockIdx.x + 1) * steps / gridDim.x;
+  int s = 0;
+  for (int64_t st = first; st < last; ++st) {
+    const int64_t e = st * kWaves + wave;
+    if (e >= entries) break;
+    const int g = (int)(e % a.hkv);
+    const int pair = (int)(e / a.hkv);
+    if (st == first) {
+      // largest s with cum[s] <= pair (sequences without splits have cum[s] == cum[s+1])
+      int lo = 0, hi = a.num_seqs - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cum[mid] <= pair) lo = mid; else hi = mid - 1;
       }
+      s = lo;
     }
-    const float inv = 1.0f / den;
-    const int64_t base = (int64_t)s * out_st + (int64_t)(g * G + h) * out_sh;
+    while (cum[s + 1] <= pair) ++s;
+    const int L = clamped_len(a, s);
+    decode_item<KVT, D, G, QT>(a, s, pair - cum[s], g, L, num_splits(L, a.split_tokens), lane);
+  }
+}
+
+// Log-sum-exp merge of the split partials of one (sequence, query head) per 256-thread
+// workgroup: out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M), M = max_i lse_i. A
+// separate launch orders it after every split (a device-scope fence in each split
+// wave instead would write back and invalidate the L2 once per wave).
+// Thread = 16 * grp + c: c owns head dims [c*D/16, (c+1)*D/16), grp (0..15) takes
+// splits grp, grp+16, ...; loads of four such splits are issued together and kept
+// as a running (max, sum, acc), then the 16 groups are combined (shuffles, then LDS).
+constexpr int kMergeThreads = 256;
+
+template <int D, int QT>
+__global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(
+    void* __restrict__ out, int64_t out_st, int64_t out_sh, int q_heads,
+    const int32_t* __restrict__ context_lens, int max_context_len, int split_tokens,
+    int max_splits, const float* __restrict__ ws_o, const float* __restrict__ ws_lse) {
+  constexpr int EV = D / 16;
+  constexpr int GROUPS = kMergeThreads / 16;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  constexpr int UNROLL = 4;
+  const int h = blockIdx.x % q_heads;
+  const int s = blockIdx.x / q_heads;
+  const int L = min(context_lens[s], max_context_len);
+  const int nsplit = L > 0 ? (L + split_tokens - 1) / split_tokens : 0;
+  if (nsplit <= 1) return;  // written directly by the split kernel (uniform exit)
+  const int tid = threadIdx.x;
+  const int grp = tid >> 4;
+  const int c = tid & 15;
+  const int64_t row0 = ((int64_t)s * q_heads + h) * max_splits;
+  float m = NEG_INF, den = 0.0f, acc[EV];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int d = lane + 64 * e;
-      if constexpr (QT == kF32) ((float*)out)[base + d] = acc[e] * inv;
-      else ((uint16_t*)out)[base + d] = f32_to_bf16(acc[e] * inv);
+  for (int e = 0; e < EV; ++e) acc[e] = 0.0f;
+  for (int i0 = grp; i0 < nsplit; i0 += GROUPS * UNROLL) {
+    float lse[UNROLL];
+    float o[UNROLL][EV];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int i = i0 + GROUPS * u;
+      const bool ok = i < nsplit;
+      lse[u] = ok ? ws_lse[row0 + i] : NEG_INF;
+      const float* op = ws_o + (row0 + (ok ? i : i0)) * D + c * EV;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) o[u][e] = op[e];
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      if (lse[u] == NEG_INF) continue;
+      const float m_new = fmaxf(m, lse[u]);
+      const float a = fast_exp2(m - m_new);  // 0 while m is -inf
+      const float w = fast_exp2(lse[u] - m_new);
+      den = fmaf(den, a, w);
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] = fmaf(acc[e], a, w * o[u][e]);
+      m = m_new;
     }
   }
-  // every split of this group has arrived: leave the counter at zero for the next call
-  if (lane == 0) *counter = 0;
+  // combine groups: the four of a wave by shuffles, then the four waves through LDS
+  auto combine = [&](float m_o, float d_o, const float* a_o) {
+    const float m_new = fmaxf(m, m_o);
+    const float a = m == NEG_INF ? 0.0f : fast_exp2(m - m_new);
+    const float b = m_o == NEG_INF ? 0.0f : fast_exp2(m_o - m_new);
+    den = den * a + d_o * b;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] = acc[e] * a + a_o[e] * b;
+    m = m_new;
+  };
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    float a_o[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) a_o[e] = __shfl_xor(acc[e], off);
+    const float m_o = __shfl_xor(m, off);
+    const float d_o = __shfl_xor(den, off);
+    combine(m_o, d_o, a_o);
+  }
+  __shared__ float part[kMergeThreads / 64][16][EV + 2];
+  const int wave = tid >> 6;
+  if ((tid & 63) < 16) {
+    part[wave][c][0] = m;
+    part[wave][c][1] = den;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) part[wave][c][2 + e] = acc[e];
+  }
+  __syncthreads();
+  if (tid >= 16) return;
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) combine(part[w][c][0], part[w][c][1], &part[w][c][2]);
+  const float inv = 1.0f / den;
+  const int64_t base = (int64_t)s * out_st + (int64_t)h * out_sh + c * EV;
+#pragma unroll
+  for (int e = 0; e < EV; ++e) {
+    if constexpr (QT == kF32) ((float*)out)[base + e] = acc[e] * inv;
+    else ((uint16_t*)out)[base + e] = f32_to_bf16(acc[e] * inv);
+  }
+}
+
+// Resident workgroups of a kernel on the whole device (CUs x workgroups per CU).
+template <typename K>
+static int64_t resident_workgroups(K kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kWaves, 0) !=
+          hipSuccess ||
+      cus <= 0 || per_cu <= 0)
+    return 1024;
+  return (int64_t)cus * per_cu;
 }
 
 template <int KVT, int D, int G, int QT>
 static void launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream) {
-  const int splits_per_row = (a.max_splits + kWaves - 1) / kWaves;
-  const int64_t grid = (int64_t)splits_per_row * pool.kv_heads * a.num_seqs;
-  decode_split_kernel<KVT, D, G, QT><<<(unsigned)grid, 64 * kWaves, 0, stream>>>(
-      (const char*)pool.k, (const char*)pool.v, pool.k_scale, pool.v_scale, pool.num_blocks,
-      pool.kv_heads, a.out, a.out_st, a.out_sh, a.q, a.q_st, a.q_sh, a.num_seqs,
-      splits_per_row, a.block_tables, a.max_blocks_per_seq, a.context_lens,
-      a.max_context_len, a.scale * kLog2e, a.split_tokens, a.max_splits, a.ws_o, a.ws_lse,
-      a.counters);
+  SplitArgs sa;
+  sa.kpool = (const char*)pool.k;
+  sa.vpool = (const char*)pool.v;
+  sa.kscale = pool.k_scale;
+  sa.vscale = pool.v_scale;
+  sa.num_blocks = pool.num_blocks;
+  sa.hkv = pool.kv_heads;
+  sa.out = a.out;
+  sa.out_st = a.out_st;
+  sa.out_sh = a.out_sh;
+  sa.q = a.q;
+  sa.q_st = a.q_st;
+  sa.q_sh = a.q_sh;
+  sa.num_seqs = a.num_seqs;
+  sa.block_tables = a.block_tables;
+  sa.max_blocks_per_seq = a.max_blocks_per_seq;
+  sa.context_lens = a.context_lens;
+  sa.max_context_len = a.max_context_len;
+  sa.scale_log2 = a.scale * kLog2e;
+  sa.split_tokens = a.split_tokens;
+  sa.max_splits = a.max_splits;
+  sa.ws_o = a.ws_o;
+  sa.ws_lse = a.ws_lse;
+  const int qe = QT == kF32 ? 4 : 2;
+  auto al = [](const void* p, int64_t st, int64_t sh, int e) {
+    return ((uintptr_t)p & 15u) == 0 && (st * e) % 16 == 0 && (sh * e) % 16 == 0;
+  };
+  sa.q_aligned = al(a.q, a.q_st, a.q_sh, qe);
+  sa.out_aligned = al(a.out, a.out_st, a.out_sh, qe);
+  const int64_t items = (int64_t)a.num_seqs * a.max_splits * pool.kv_heads;
+  const int64_t steps = (items + kWaves - 1) / kWaves;  // upper bound of workgroup steps
+  if (a.num_seqs <= kMaxCompactSeqs) {
+    auto kern = decode_compact_kernel<KVT, D, G, QT>;
+    const int64_t grid = std::min(steps, resident_workgroups(kern));
+    kern<<<(unsigned)grid, 64 * kWaves, 0, stream>>>(sa);
+  } else {
+    decode_split_kernel<KVT, D, G, QT><<<(unsigned)steps, 64 * kWaves, 0, stream>>>(sa);
+  }
+  if (a.max_splits > 1)
+    decode_merge_kernel<D, QT><<<(unsigned)((int64_t)a.num_seqs * a.q_heads), kMergeThreads, 0,
+                                 stream>>>(
+        a.out, a.out_st, a.out_sh, a.q_heads, a.context_lens, a.max_context_len,
+        a.split_tokens, a.max_splits, a.ws_o, a.ws_lse);
 }
 
 template <int KVT, int D, int QT>

@@ -9,7 +9,6 @@
 namespace pa {
 
 constexpr int kBlockSize = 16;
-constexpr int kDefaultSplitTokens = 256;
 
 int launch_store(const pa_kv_pool_t& pool, const void* k, const void* v, int src_dtype,
                  int64_t num_tokens, int64_t k_st, int64_t k_sh, int64_t v_st, int64_t v_sh,
@@ -28,14 +27,10 @@ struct DecodeArgs {
   float scale;
   int split_tokens;
   int max_splits;
-  int* counters;  // [num_seqs * kv_heads] arrival counters, zero between calls
   float* ws_o;    // [num_seqs, q_heads, max_splits, head_dim]
   float* ws_lse;  // [num_seqs, q_heads, max_splits]
 };
 
-// Workspace layout of pa_decode: counters (num_seqs * q_heads ints, 256-byte aligned
-// size), then the partial outputs, then the partial log-sum-exps.
-size_t decode_counter_bytes(int num_seqs, int q_heads);
 
 int launch_decode(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream);
 

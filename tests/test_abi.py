@@ -93,21 +93,28 @@ def test_decode_validation(lib):
     assert decode(lib, p, maxctx=0) == INVALID
     assert decode(lib, p, split=8) == INVALID                # not a multiple of 16
     assert decode(lib, p, split=2048) == INVALID             # beyond 1024
-    # 128 tokens at the default split of 256 need no workspace; split 16 needs one
+    # split 16 over up to 128 tokens needs a workspace
     assert decode(lib, p, split=16, ws=0) == WORKSPACE
-    need = lib.pa_decode_workspace_bytes(2, 12, 128, 128, 16)
-    assert need == 256 + 2 * 12 * 8 * 129 * 4        # counters (rounded) + partials
+    need = lib.pa_decode_workspace_bytes(2, 12, 2, 128, 128, 16)
+    assert need == 2 * 12 * 8 * 129 * 4
     assert decode(lib, p, split=16, ws=0xC000, wsb=need - 1) == WORKSPACE
 
 
-def test_workspace_bytes(lib):
-    d = lib.pa_decode_default_split_tokens()
-    assert d % 16 == 0 and 16 <= d <= 1024
-    assert lib.pa_decode_workspace_bytes(4, 8, 64, d, 0) == 0
-    assert lib.pa_decode_workspace_bytes(4, 8, 64, d + 1, 0) == 256 + 4 * 8 * 2 * 65 * 4
-    assert lib.pa_decode_workspace_bytes(40, 8, 64, d + 1, 0) == 1280 + 40 * 8 * 2 * 65 * 4
-    assert lib.pa_decode_workspace_bytes(0, 8, 64, 100, 0) == 0
-    assert lib.pa_decode_workspace_bytes(4, 8, 64, 100, -16) == 0
+def test_default_split_and_workspace_bytes(lib):
+    ds = lib.pa_decode_default_split_tokens
+    assert ds(8, 2, 3200) == 32            # small batch: short splits
+    assert ds(8, 2, 8192) == 64
+    assert ds(64, 2, 8192) == 512
+    assert ds(256, 8, 32768) == 512        # capped
+    assert ds(16, 8, 8192) == 512
+    assert ds(8, 8, 8192) == 256
+    assert ds(0, 2, 100) == 0
+    wb = lib.pa_decode_workspace_bytes
+    assert wb(4, 8, 2, 64, 32, 0) == 0      # one split of 32 covers every context
+    assert wb(4, 8, 2, 64, 65, 0) == 4 * 8 * 3 * 65 * 4
+    assert wb(4, 8, 2, 64, 65, 32) == 4 * 8 * 3 * 65 * 4
+    assert wb(0, 8, 2, 64, 100, 0) == 0
+    assert wb(4, 8, 2, 64, 100, -16) == 0
 
 
 def prefill(lib, pool, q_dtype=pa.PA_BF16, B=2, T=10, maxq=8, Hq=12, maxb=8, maxctx=128,
