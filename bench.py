@@ -243,7 +243,7 @@ def extra_fp8_decode(torch, pa, W, dev, reps=30, copies=2, split_tokens=0):
             "seqs_per_s": round(B / ((ms + ms_store) / 1e3), 1)}
 
 
-def extra_prefill(torch, pa, W, dev, reps=30):
+def extra_prefill(torch, pa, W, dev, reps=30, split_tokens=0):
     case = W.make(3)
     pool = pa.KVPool.empty(case.num_blocks, case.Hkv, case.D, "bf16", dev)
     W.fill_device_normal_(pool.k, 31)
@@ -257,10 +257,13 @@ def extra_prefill(torch, pa, W, dev, reps=30):
     bt = torch.from_numpy(case.block_tables).to(dev)
     ctx = torch.from_numpy(case.context_lens).to(dev)
     out = torch.empty_like(q)
+    ws = pa.varlen_prefill_workspace(q.shape[0], case.Hq, case.D, case.max_context_len,
+                                     split_tokens, device=dev)
 
     def run():
         pa.varlen_prefill(q, cu, pool, bt, ctx, case.scale, max_q_len=case.max_q_len,
-                          max_context_len=case.max_context_len, out=out)
+                          max_context_len=case.max_context_len, split_tokens=split_tokens,
+                          out=out, workspace=ws)
 
     g = capture(torch, run)
     gs = capture(torch, lambda: pa.store_kv(pool, kn, vn, slots))

@@ -171,7 +171,7 @@ int32_t pa_decode_default_split_tokens(int32_t num_seqs, int32_t kv_heads,
  *                ceil(L / block_size) are never read.
  *   context_lens [num_seqs] int32, each in [1, max_context_len].
  *   max_context_len  host-side upper bound of context_lens (sizes the grid).
- *   scale        softmax scale (e.g. 1/sqrt(head_dim)).
+ *   scale        softmax scale, finite and > 0 (e.g. 1/sqrt(head_dim)).
  *   split_tokens tokens per split-K work item: a positive multiple of block_size, at
  *                most 1024, or 0 for pa_decode_default_split_tokens(num_seqs,
  *                kv_heads, max_context_len). With a given split length the split of
@@ -211,17 +211,29 @@ int pa_decode(void *out, int64_t out_stride_tok, int64_t out_stride_head, const 
  *   cu_seqlens   [num_seqs+1] int32, cu[0] = 0, non-decreasing, cu[num_seqs] =
  *                total_tokens. n_s == 0 is allowed (no rows).
  *   max_q_len    host-side upper bound of n_s (sizes the grid).
+ *   split_tokens keys per work item: 0 = 1024, else a positive multiple of 64. A row
+ *                tile whose visible keys exceed it is split into key chunks handled
+ *                in parallel and merged by log-sum-exp; results depend bitwise only
+ *                on this value and each sequence's own (n_s, context_lens[s]).
+ *   workspace    device scratch of at least pa_varlen_prefill_workspace_bytes(...)
+ *                bytes for the same (total_tokens, q_heads, head_dim, max_context_len,
+ *                split_tokens); may be NULL when that is 0; contents on entry ignored.
  *   Other arguments as in pa_decode. A chunk of length 1 is a decode row.
- * Supported dtypes: (q BF16, pool BF16) and (q BF16, pool FP8_E4M3). QK^T and PV run
- * on the matrix cores with bf16 operands (P rounded to bf16) and fp32 accumulation.
+ * Supported dtypes: (q BF16, pool BF16). QK^T and PV run on the matrix cores with
+ * bf16 operands (P rounded to bf16) and fp32 accumulation.
  */
+size_t pa_varlen_prefill_workspace_bytes(int64_t total_tokens, int32_t q_heads,
+                                         int32_t head_dim, int32_t max_context_len,
+                                         int32_t split_tokens);
+
 int pa_varlen_prefill(void *out, int64_t out_stride_tok, int64_t out_stride_head,
                       const void *q, int64_t q_stride_tok, int64_t q_stride_head,
                       int32_t q_dtype, const int32_t *cu_seqlens, int32_t num_seqs,
                       int64_t total_tokens, int32_t max_q_len, int32_t q_heads,
                       const pa_kv_pool_t *pool, const int32_t *block_tables,
                       int32_t max_blocks_per_seq, const int32_t *context_lens,
-                      int32_t max_context_len, float scale, void *stream);
+                      int32_t max_context_len, float scale, int32_t split_tokens,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -55,9 +55,10 @@ SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32,
                                  ctypes.POINTER(_Pool), _P, _I32, _P, _I32, _F, _I32, _P, _SZ,
                                  _P]),
+    "pa_varlen_prefill_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
     "pa_varlen_prefill": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _P, _I32, _I64,
                                          _I32, _I32, ctypes.POINTER(_Pool), _P, _I32, _P, _I32,
-                                         _F, _P]),
+                                         _F, _I32, _P, _SZ, _P]),
 }
 
 
@@ -211,9 +212,25 @@ def decode(q, pool, block_tables, context_lens, scale, max_context_len=None, spl
     return out
 
 
+def varlen_prefill_workspace_bytes(total_tokens, q_heads, head_dim, max_context_len,
+                                   split_tokens=0):
+    return int(lib().pa_varlen_prefill_workspace_bytes(total_tokens, q_heads, head_dim,
+                                                       max_context_len, split_tokens))
+
+
+def varlen_prefill_workspace(total_tokens, q_heads, head_dim, max_context_len, split_tokens=0,
+                             device="cuda"):
+    """A workspace for varlen_prefill() calls of these sizes (and split length)."""
+    need = varlen_prefill_workspace_bytes(total_tokens, q_heads, head_dim, max_context_len,
+                                          split_tokens)
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+
 def varlen_prefill(q, cu_seqlens, pool, block_tables, context_lens, scale, max_q_len=None,
-                   max_context_len=None, out=None):
-    """Varlen causal prefill: q [T, Hq, D] with chunks cu_seqlens [B+1] -> out [T, Hq, D]."""
+                   max_context_len=None, split_tokens=0, out=None, workspace=None):
+    """Varlen causal prefill: q [T, Hq, D] with chunks cu_seqlens [B+1] -> out [T, Hq, D].
+    split_tokens: keys per work item (0 = library default); workspace: optional
+    preallocated uint8 tensor (varlen_prefill_workspace())."""
     _meta(block_tables, context_lens)
     _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1
           and cu_seqlens.is_contiguous(), "cu_seqlens must be contiguous int32 [B+1]")
@@ -226,10 +243,14 @@ def varlen_prefill(q, cu_seqlens, pool, block_tables, context_lens, scale, max_q
     if out is None:
         out = torch.empty((T, Hq, D), dtype=q.dtype, device=q.device)
     qs, os_ = _rows3(q, "q"), _rows3(out, "out")
+    need = varlen_prefill_workspace_bytes(T, Hq, D, max_context_len, split_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pa_varlen_prefill(_ptr(out), os_[0], os_[1], _ptr(q), qs[0], qs[1],
                                    _DTYPE_CODE[q.dtype], _ptr(cu_seqlens), B, T, int(max_q_len),
                                    Hq, pool.struct, _ptr(block_tables), block_tables.shape[1],
                                    _ptr(context_lens), int(max_context_len), float(scale),
-                                   _stream()),
+                                   int(split_tokens), _ptr(workspace), wbytes, _stream()),
            "pa_varlen_prefill")
     return out

@@ -117,6 +117,7 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
     return PA_ERR_INVALID_ARG;
   if (split_tokens < 0 || split_tokens % kBlockSize != 0 || split_tokens > kMaxSplitTokens)
     return PA_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || scale > 3.0e38f) return PA_ERR_INVALID_ARG;  // finite, positive
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
   if (max_blocks_per_seq <= 0 || max_context_len <= 0 ||
@@ -153,13 +154,26 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
   return launched(pa::launch_decode(*pool, a, (hipStream_t)stream));
 }
 
+size_t pa_varlen_prefill_workspace_bytes(int64_t total_tokens, int32_t q_heads,
+                                         int32_t head_dim, int32_t max_context_len,
+                                         int32_t split_tokens) {
+  if (total_tokens <= 0 || q_heads <= 0 || head_dim <= 0 || max_context_len <= 0 ||
+      split_tokens < 0 || split_tokens % 64 != 0)
+    return 0;
+  const int split = split_tokens == 0 ? pa::kPrefillDefaultSplit : split_tokens;
+  const int64_t chunks = ((int64_t)max_context_len + split - 1) / split;
+  if (chunks <= 1) return 0;
+  return (size_t)total_tokens * q_heads * chunks * (head_dim + 1) * sizeof(float);
+}
+
 int pa_varlen_prefill(void* out, int64_t out_stride_tok, int64_t out_stride_head,
                       const void* q, int64_t q_stride_tok, int64_t q_stride_head,
                       int32_t q_dtype, const int32_t* cu_seqlens, int32_t num_seqs,
                       int64_t total_tokens, int32_t max_q_len, int32_t q_heads,
                       const pa_kv_pool_t* pool, const int32_t* block_tables,
                       int32_t max_blocks_per_seq, const int32_t* context_lens,
-                      int32_t max_context_len, float scale, void* stream) {
+                      int32_t max_context_len, float scale, int32_t split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   int status = PA_OK;
   if (!pool_shape_ok(pool, &status)) return status;
   if (num_seqs < 0 || total_tokens < 0 || q_heads <= 0 || q_heads % pool->kv_heads != 0)
@@ -169,14 +183,23 @@ int pa_varlen_prefill(void* out, int64_t out_stride_tok, int64_t out_stride_head
   if (pool->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (out_stride_tok < 0 || out_stride_head < 0 || q_stride_tok < 0 || q_stride_head < 0)
     return PA_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || scale > 3.0e38f) return PA_ERR_INVALID_ARG;  // finite, positive
   if (num_seqs == 0 || total_tokens == 0) return PA_OK;
   if (!out || !q || !cu_seqlens || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
   if (max_q_len <= 0 || max_blocks_per_seq <= 0 || max_context_len <= 0 ||
       max_q_len > max_context_len ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlockSize)
     return PA_ERR_INVALID_ARG;
+  if (split_tokens < 0 || split_tokens % 64 != 0) return PA_ERR_INVALID_ARG;
+  const int split = split_tokens == 0 ? pa::kPrefillDefaultSplit : split_tokens;
+  const int max_chunks = (max_context_len + split - 1) / split;
+  const size_t need = pa_varlen_prefill_workspace_bytes(total_tokens, q_heads, pool->head_dim,
+                                                        max_context_len, split);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
   const int64_t tiles = ((int64_t)max_q_len * (q_heads / pool->kv_heads) + 127) / 128;
-  if (tiles * pool->kv_heads * num_seqs >= (int64_t)1 << 31) return PA_ERR_UNSUPPORTED;
+  if (tiles * max_chunks * pool->kv_heads * num_seqs >= (int64_t)1 << 31 ||
+      total_tokens * q_heads >= (int64_t)1 << 31)
+    return PA_ERR_UNSUPPORTED;
 
   pa::PrefillArgs a;
   a.out = out;
@@ -195,6 +218,11 @@ int pa_varlen_prefill(void* out, int64_t out_stride_tok, int64_t out_stride_head
   a.context_lens = context_lens;
   a.max_context_len = max_context_len;
   a.scale = scale;
+  a.split_keys = split;
+  a.max_chunks = max_chunks;
+  a.ws_o = (float*)workspace;
+  a.ws_lse = need > 0 ? a.ws_o + (size_t)total_tokens * q_heads * max_chunks * pool->head_dim
+                      : nullptr;
   return launched(pa::launch_prefill(*pool, a, (hipStream_t)stream));
 }
 

@@ -48,7 +48,13 @@ struct PrefillArgs {
   const int32_t* context_lens;
   int max_context_len;
   float scale;
+  int split_keys;  // keys per work item, multiple of 64
+  int max_chunks;  // ceil(max_context_len / split_keys)
+  float* ws_o;     // [total_tokens, q_heads, max_chunks, head_dim] when max_chunks > 1
+  float* ws_lse;   // [total_tokens, q_heads, max_chunks]
 };
+
+constexpr int kPrefillDefaultSplit = 1024;
 
 int launch_prefill(const pa_kv_pool_t& pool, const PrefillArgs& a, hipStream_t stream);
 

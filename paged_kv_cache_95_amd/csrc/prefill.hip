@@ -22,6 +22,11 @@
 //    group of 16), so each A operand is one 16-byte LDS read.
 //  * The causal mask is applied only on tiles that reach past the wave's first row.
 //    Keys past the context are zero-filled in LDS (never multiplied in as garbage).
+//  * Long key ranges are split into chunks of split_keys keys handled by separate
+//    workgroups (the critical path is otherwise the row tile with the longest prefix);
+//    split tiles write (o, lse) partials and a small kernel merges them by
+//    log-sum-exp. The next 64-key tile is fetched into registers while the current
+//    one is multiplied.
 #include "common.h"
 #include "internal.h"
 
@@ -40,14 +45,42 @@ __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
+struct PfArgs {
+  const uint16_t* kpool;
+  const uint16_t* vpool;
+  int64_t num_blocks;
+  int hkv;
+  uint16_t* out;
+  int64_t out_st, out_sh;
+  const uint16_t* q;
+  int64_t q_st, q_sh;
+  const int32_t* cu_seqlens;
+  int num_seqs;
+  int64_t total_tokens;
+  int tiles_per_seq;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int max_context_len;
+  float scale_log2;
+  bool q_aligned;    // q rows start on 16 bytes
+  bool out_aligned;  // out rows start on 8 bytes
+  int q_heads;
+  int split_keys;    // keys per work item (multiple of 64)
+  int max_chunks;    // ceil(max_context_len / split_keys)
+  float* ws_o;       // [total_tokens, q_heads, max_chunks, D] partials (max_chunks > 1)
+  float* ws_lse;     // [total_tokens, q_heads, max_chunks]
+};
+
 template <int D, int G>
-__global__ void __launch_bounds__(256) prefill_kernel(
-    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool, int64_t num_blocks,
-    int hkv, uint16_t* __restrict__ out, int64_t out_st, int64_t out_sh,
-    const uint16_t* __restrict__ q, int64_t q_st, int64_t q_sh,
-    const int32_t* __restrict__ cu_seqlens, int64_t total_tokens, int tiles_per_seq,
-    const int32_t* __restrict__ block_tables, int max_blocks_per_seq,
-    const int32_t* __restrict__ context_lens, int max_context_len, float scale_log2) {
+__global__ void __launch_bounds__(256, 2) prefill_kernel(PfArgs a) {
+  const uint16_t* __restrict__ kpool = a.kpool;
+  const uint16_t* __restrict__ vpool = a.vpool;
+  const int64_t num_blocks = a.num_blocks;
+  const int hkv = a.hkv;
+  const uint16_t* __restrict__ q = a.q;
+  const int64_t q_st = a.q_st, q_sh = a.q_sh;
+  const bool q_aligned = a.q_aligned, out_aligned = a.out_aligned;
   constexpr int KROW = D + kKPad;             // LDS K row stride (elements)
   constexpr int VROW = kPfKeys + kVPad;       // LDS V^T row stride (elements)
   constexpr int CH = D / 8;                   // 16-byte chunks per K/V row
@@ -63,25 +96,33 @@ __global__ void __launch_bounds__(256) prefill_kernel(
   const int hl = lane >> 5;     // which half of the wave (k-slot group of the MFMA)
   const int l32 = lane & 31;
 
-  // blockIdx.x -> (tile, kv head, sequence); the last (longest) tiles of a chunk first
-  const int mt = tiles_per_seq - 1 - (int)(blockIdx.x % tiles_per_seq);
-  const int rest = blockIdx.x / tiles_per_seq;
-  const int g = rest % hkv;
-  const int s = rest / hkv;
-  const int t_begin = cu_seqlens[s];
-  const int t_end = cu_seqlens[s + 1];
+  // blockIdx.x -> (row tile, key chunk, kv head, sequence); within a chunk the last
+  // (longest) row tiles come first
+  const int mt = a.tiles_per_seq - 1 - (int)(blockIdx.x % a.tiles_per_seq);
+  const int rest = blockIdx.x / a.tiles_per_seq;
+  const int chunk = rest % a.max_chunks;
+  const int rest2 = rest / a.max_chunks;
+  const int g = rest2 % hkv;
+  const int s = rest2 / hkv;
+  const int t_begin = a.cu_seqlens[s];
+  const int t_end = a.cu_seqlens[s + 1];
   // chunks outside [0, total_tokens] break the cu_seqlens contract: skip them rather
   // than read or write outside q / out
-  if (t_begin < 0 || t_end > total_tokens) return;
+  if (t_begin < 0 || t_end > a.total_tokens) return;
   const int n = t_end - t_begin;
   const int nrows = n * G;
   const int m0 = mt * kPfRows;
   if (m0 >= nrows) return;  // whole workgroup: no barrier reached yet
   // clamp to the host bound (<= max_blocks_per_seq * 16) so table reads stay in the row
-  const int L = min(context_lens[s], max_context_len);
+  const int L = min(a.context_lens[s], a.max_context_len);
   const int P = L - n;
   const int m_last = min(m0 + kPfRows, nrows) - 1;
   const int kend = P + m_last / G + 1;  // keys [0, kend) are visible to some row here
+  // this work item's key range [k_lo, k_hi)
+  const int nchunks = (kend + a.split_keys - 1) / a.split_keys;
+  if (chunk >= nchunks) return;
+  const int k_lo = chunk * a.split_keys;
+  const int k_hi = min(kend, k_lo + a.split_keys);
 
   // ---- this wave's rows
   const int mw0 = m0 + 32 * wave;
@@ -100,13 +141,18 @@ __global__ void __launch_bounds__(256) prefill_kernel(
     const uint16_t* qp = q + (int64_t)(t_begin + my_tok) * q_st + (int64_t)(g * G + my_hh) * q_sh;
 #pragma unroll
     for (int st = 0; st < DSTEPS; ++st) {
-      uint32_t w[4];
+      const int d0 = 16 * st + 8 * hl;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (row_ok && q_aligned) {
+        x = *reinterpret_cast<const uint4*>(qp + d0);
+      } else if (row_ok) {
+        uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 16 * st + 8 * hl + 2 * e;
-        w[e] = row_ok ? ((uint32_t)qp[d] | ((uint32_t)qp[d + 1] << 16)) : 0u;
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)qp[d0 + 2 * e] | ((uint32_t)qp[d0 + 2 * e + 1] << 16);
+        x = make_uint4(w[0], w[1], w[2], w[3]);
       }
-      qreg[st] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+      qreg[st] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
 
@@ -117,61 +163,102 @@ __global__ void __launch_bounds__(256) prefill_kernel(
     for (int j = 0; j < 16; ++j) oacc[dn][j] = 0.0f;
   float m_run = NEG_INF, l_run = 0.0f;
 
-  const int32_t* bt_row = block_tables + (int64_t)s * max_blocks_per_seq;
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int64_t tok_stride = (int64_t)hkv * D;  // elements between consecutive slots
 
-  const int ntiles = (kend + kPfKeys - 1) / kPfKeys;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int kbase = kt * kPfKeys;
-    __syncthreads();
-    // ---- gather K tile: row-major [key][d], 16 bytes per thread per step
+  // K tile: row-major [key][d], 16 bytes per thread per step. V tile: four consecutive
+  // keys x 8 dims per thread (written transposed). The next tile is fetched into
+  // registers while the current one is computed, then stashed into LDS.
+  constexpr int KIT = (kPfKeys * CH) / 256;   // K chunks per thread
+  // V work items: 16 key quads x CH chunks, key quad fastest, so that one wave's
+  // transposed LDS writes spread over the banks (chunk-fastest would put 8 lanes on
+  // the same bank offset)
+  const bool v_has = tid < 16 * CH;
+  const int v_kq = tid & 15, v_ch = tid >> 4;
+  uint4 kreg[KIT];
+  uint4 vreg[4];
+  // The 64 keys of tile kt are pool blocks kt*4 .. kt*4+3 of the sequence: four block
+  // ids, the same for every thread, read as uniform (scalar) loads one tile ahead.
+  auto tile_bids = [&](int kt, int (&bids)[4]) {
 #pragma unroll
-    for (int it = 0; it < (kPfKeys * CH) / 256; ++it) {
+    for (int i = 0; i < 4; ++i) {
+      const int kb = kt * 4 + i;
+      const int raw = kb * kBlockSize < L ? bt_row[kb] : -1;
+      bids[i] = (unsigned)raw < (uint64_t)num_blocks ? raw : -1;
+    }
+  };
+  auto fetch = [&](int kt, const int (&bids)[4]) {
+    const int kbase = kt * kPfKeys;
+    // a tile fully inside the context with valid block ids (the common case) needs no
+    // per-element guards
+    const bool full = kbase + kPfKeys <= L && bids[0] >= 0 && bids[1] >= 0 &&
+                      bids[2] >= 0 && bids[3] >= 0;
+    const int vbid = bids[v_kq >> 2];
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
       const int w = tid + 256 * it;
       const int key = w / CH, ch = w % CH;
       const int ka = kbase + key;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (ka < L) {
-        const int bid = bt_row[ka >> 4];
-        if ((unsigned)bid < (uint64_t)num_blocks) {
-          const int64_t off = ((int64_t)bid * kBlockSize + (ka & 15)) * tok_stride + (int64_t)g * D + ch * 8;
-          x = *reinterpret_cast<const uint4*>(kpool + off);
-        }
+      const int bid = bids[key >> 4];
+      const int64_t off = ((int64_t)bid * kBlockSize + (ka & 15)) * tok_stride + (int64_t)g * D + ch * 8;
+      if (full) {
+        kreg[it] = *reinterpret_cast<const uint4*>(kpool + off);
+      } else {
+        kreg[it] = make_uint4(0, 0, 0, 0);
+        if (ka < L && bid >= 0) kreg[it] = *reinterpret_cast<const uint4*>(kpool + off);
       }
-      *reinterpret_cast<uint4*>(&Ks[key * KROW + ch * 8]) = x;
     }
-    // ---- gather V tile: four consecutive keys x 8 dims per thread, written transposed
-    for (int w = tid; w < 16 * CH; w += 256) {
-      const int kq = w / CH, ch = w % CH;
-      uint4 rows[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ka = kbase + 4 * kq + r;
-        rows[r] = make_uint4(0, 0, 0, 0);
-        if (ka < L) {
-          const int bid = bt_row[ka >> 4];
-          if ((unsigned)bid < (uint64_t)num_blocks) {
-            const int64_t off = ((int64_t)bid * kBlockSize + (ka & 15)) * tok_stride + (int64_t)g * D + ch * 8;
-            rows[r] = *reinterpret_cast<const uint4*>(vpool + off);
-          }
-        }
+    for (int r = 0; r < 4; ++r) {
+      const int ka = kbase + 4 * v_kq + r;
+      const int64_t off = ((int64_t)vbid * kBlockSize + (ka & 15)) * tok_stride + (int64_t)g * D + v_ch * 8;
+      if (full) {
+        vreg[r] = v_has ? *reinterpret_cast<const uint4*>(vpool + off) : make_uint4(0, 0, 0, 0);
+      } else {
+        vreg[r] = make_uint4(0, 0, 0, 0);
+        if (v_has && ka < L && vbid >= 0) vreg[r] = *reinterpret_cast<const uint4*>(vpool + off);
       }
-      const int pos = vt_pos(4 * kq);
-      const uint32_t* r0 = &rows[0].x;
-      const uint32_t* r1 = &rows[1].x;
-      const uint32_t* r2 = &rows[2].x;
-      const uint32_t* r3 = &rows[3].x;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int w = tid + 256 * it;
+      const int key = w / CH, ch = w % CH;
+      *reinterpret_cast<uint4*>(&Ks[key * KROW + ch * 8]) = kreg[it];
+    }
+    if (v_has) {
+      const int pos = vt_pos(4 * v_kq);
+      const uint32_t* r0 = &vreg[0].x;
+      const uint32_t* r1 = &vreg[1].x;
+      const uint32_t* r2 = &vreg[2].x;
+      const uint32_t* r3 = &vreg[3].x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint2 lo = make_uint2(__builtin_amdgcn_perm(r1[e], r0[e], 0x05040100u),
                                     __builtin_amdgcn_perm(r3[e], r2[e], 0x05040100u));
         const uint2 hi = make_uint2(__builtin_amdgcn_perm(r1[e], r0[e], 0x07060302u),
                                     __builtin_amdgcn_perm(r3[e], r2[e], 0x07060302u));
-        *reinterpret_cast<uint2*>(&Vt[(ch * 8 + 2 * e) * VROW + pos]) = lo;
-        *reinterpret_cast<uint2*>(&Vt[(ch * 8 + 2 * e + 1) * VROW + pos]) = hi;
+        *reinterpret_cast<uint2*>(&Vt[(v_ch * 8 + 2 * e) * VROW + pos]) = lo;
+        *reinterpret_cast<uint2*>(&Vt[(v_ch * 8 + 2 * e + 1) * VROW + pos]) = hi;
       }
     }
+  };
+
+  const int kt0 = k_lo / kPfKeys;
+  const int ntiles = (k_hi + kPfKeys - 1) / kPfKeys;
+  int bids[4], bids_next[4];
+  if (kt0 < ntiles) {
+    tile_bids(kt0, bids);
+    fetch(kt0, bids);
+  }
+  for (int kt = kt0; kt < ntiles; ++kt) {
+    const int kbase = kt * kPfKeys;
+    if (kt + 1 < ntiles) tile_bids(kt + 1, bids_next);
+    __syncthreads();  // every wave is done reading the previous tile
+    stash();
     __syncthreads();
+    if (kt + 1 < ntiles) fetch(kt + 1, bids_next);
     if (!wave_active || kbase > wave_last_limit) continue;
 
     // ---- S^T = K Q^T for keys kbase + [0, 32) and + [32, 64)
@@ -188,12 +275,13 @@ __global__ void __launch_bounds__(256) prefill_kernel(
     }
     // ---- online softmax; lane holds keys kbase + 32nn + 8(j/4) + 4hl + j%4 of its row
     const bool need_mask = kbase + kPfKeys - 1 > wave_first_limit;
+    // raw scores: the (positive) scale is applied once, fused into the exponent
     float tmax = NEG_INF;
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float x = sacc[nn][j] * scale_log2;
+        float x = sacc[nn][j];
         if (need_mask) {
           const int key = kbase + 32 * nn + 8 * (j >> 2) + 4 * hl + (j & 3);
           x = key <= my_limit ? x : NEG_INF;
@@ -202,7 +290,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(
         tmax = fmaxf(tmax, x);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
+    const float sl2 = a.scale_log2;
+    const float m_new = fmaxf(m_run, tmax * sl2);
     // rows past the chunk (my_limit = -1) see no key at all: keep them at zero
     const float m_use = m_new == NEG_INF ? 0.0f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
@@ -214,7 +303,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(
       float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pv[i] = fast_exp2(sacc[t >> 1][8 * (t & 1) + i] - m_use);
+        pv[i] = fast_exp2(fmaf(sacc[t >> 1][8 * (t & 1) + i], sl2, -m_use));
         psum += pv[i];
       }
 #pragma unroll
@@ -239,8 +328,27 @@ __global__ void __launch_bounds__(256) prefill_kernel(
 
   if (!row_ok) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (nchunks > 1) {
+    // partial over this key chunk: normalised o and log2-sum-exp; a row that saw no
+    // key here (all past its causal limit) gets lse = -inf and weighs nothing
+    const bool any = l_tot > 0.0f;
+    const float inv = any ? 1.0f / l_tot : 0.0f;
+    const int64_t row = ((int64_t)(t_begin + my_tok) * a.q_heads + g * G + my_hh) * a.max_chunks + chunk;
+    float* wo = a.ws_o + row * D;
+#pragma unroll
+    for (int dn = 0; dn < DT; ++dn)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int d = 32 * dn + 8 * jq + 4 * hl;
+        *reinterpret_cast<float4*>(wo + d) =
+            make_float4(oacc[dn][4 * jq] * inv, oacc[dn][4 * jq + 1] * inv,
+                        oacc[dn][4 * jq + 2] * inv, oacc[dn][4 * jq + 3] * inv);
+      }
+    if (hl == 0) a.ws_lse[row] = any ? m_run + __log2f(l_tot) : -__builtin_huge_valf();
+    return;
+  }
   const float inv = 1.0f / l_tot;
-  uint16_t* op = out + (int64_t)(t_begin + my_tok) * out_st + (int64_t)(g * G + my_hh) * out_sh;
+  uint16_t* op = a.out + (int64_t)(t_begin + my_tok) * a.out_st + (int64_t)(g * G + my_hh) * a.out_sh;
 #pragma unroll
   for (int dn = 0; dn < DT; ++dn)
 #pragma unroll
@@ -250,22 +358,100 @@ __global__ void __launch_bounds__(256) prefill_kernel(
                           ((uint32_t)f32_to_bf16(oacc[dn][4 * jq + 1] * inv) << 16);
       const uint32_t w1 = (uint32_t)f32_to_bf16(oacc[dn][4 * jq + 2] * inv) |
                           ((uint32_t)f32_to_bf16(oacc[dn][4 * jq + 3] * inv) << 16);
-      op[d] = (uint16_t)w0;
-      op[d + 1] = (uint16_t)(w0 >> 16);
-      op[d + 2] = (uint16_t)w1;
-      op[d + 3] = (uint16_t)(w1 >> 16);
+      if (out_aligned) {
+        *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
+      } else {
+        op[d] = (uint16_t)w0;
+        op[d + 1] = (uint16_t)(w0 >> 16);
+        op[d + 2] = (uint16_t)w1;
+        op[d + 3] = (uint16_t)(w1 >> 16);
+      }
     }
 }
 
+// Merge of the key-chunk partials of one (token, query head) per wavefront, for tokens
+// whose row tile was split: out = sum_c 2^(lse_c - M) o_c / sum_c 2^(lse_c - M).
+template <int D>
+__global__ void __launch_bounds__(64) prefill_merge_kernel(PfArgs a) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int h = (int)(blockIdx.x % a.q_heads);
+  const int64_t t = blockIdx.x / a.q_heads;
+  const int G = a.q_heads / a.hkv;
+  // sequence of token t: the first s with cu[s + 1] > t
+  int lo = 0, hi = a.num_seqs;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_seqlens[mid + 1] <= t) lo = mid + 1; else hi = mid;
+  }
+  const int s = lo;
+  if (s >= a.num_seqs) return;
+  const int t_begin = a.cu_seqlens[s], t_end = a.cu_seqlens[s + 1];
+  if (t_begin < 0 || t_end > a.total_tokens || t < t_begin) return;
+  const int n = t_end - t_begin;
+  const int nrows = n * G;
+  const int i = (int)(t - t_begin);
+  const int m = i * G + h % G;
+  const int m0 = (m / kPfRows) * kPfRows;
+  const int m_last = min(m0 + kPfRows, nrows) - 1;
+  const int L = min(a.context_lens[s], a.max_context_len);
+  const int kend = L - n + m_last / G + 1;
+  const int nch = (kend + a.split_keys - 1) / a.split_keys;
+  if (nch <= 1) return;  // written directly by the prefill kernel
+  const int lane = threadIdx.x;
+  const int64_t row0 = (t * a.q_heads + h) * a.max_chunks;
+  constexpr int PER = D / 64;
+  float mx = NEG_INF;
+  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.ws_lse[row0 + c]);
+  float acc[PER], den = 0.0f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+  for (int c = 0; c < nch; ++c) {
+    const float lse = a.ws_lse[row0 + c];
+    if (lse == NEG_INF) continue;
+    const float w = fast_exp2(lse - mx);
+    den += w;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, a.ws_o[(row0 + c) * D + lane + 64 * e], acc[e]);
+  }
+  const float inv = 1.0f / den;
+  uint16_t* op = a.out + t * a.out_st + (int64_t)h * a.out_sh;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) op[lane + 64 * e] = f32_to_bf16(acc[e] * inv);
+}
+
 template <int D, int G>
-static void launch_prefill_t(const pa_kv_pool_t& pool, const PrefillArgs& a, hipStream_t stream) {
-  const int tiles = (int)(((int64_t)a.max_q_len * G + kPfRows - 1) / kPfRows);
-  const int64_t grid = (int64_t)tiles * pool.kv_heads * a.num_seqs;
-  prefill_kernel<D, G><<<(unsigned)grid, 256, 0, stream>>>(
-      (const uint16_t*)pool.k, (const uint16_t*)pool.v, pool.num_blocks, pool.kv_heads,
-      (uint16_t*)a.out, a.out_st, a.out_sh, (const uint16_t*)a.q, a.q_st, a.q_sh, a.cu_seqlens,
-      a.total_tokens, tiles, a.block_tables, a.max_blocks_per_seq, a.context_lens,
-      a.max_context_len, a.scale * kLog2e);
+static void launch_prefill_t(const pa_kv_pool_t& pool, const PrefillArgs& pa_, hipStream_t stream) {
+  PfArgs a;
+  a.kpool = (const uint16_t*)pool.k;
+  a.vpool = (const uint16_t*)pool.v;
+  a.num_blocks = pool.num_blocks;
+  a.hkv = pool.kv_heads;
+  a.out = (uint16_t*)pa_.out;
+  a.out_st = pa_.out_st;
+  a.out_sh = pa_.out_sh;
+  a.q = (const uint16_t*)pa_.q;
+  a.q_st = pa_.q_st;
+  a.q_sh = pa_.q_sh;
+  a.cu_seqlens = pa_.cu_seqlens;
+  a.num_seqs = pa_.num_seqs;
+  a.total_tokens = pa_.total_tokens;
+  a.tiles_per_seq = (int)(((int64_t)pa_.max_q_len * G + kPfRows - 1) / kPfRows);
+  a.block_tables = pa_.block_tables;
+  a.max_blocks_per_seq = pa_.max_blocks_per_seq;
+  a.context_lens = pa_.context_lens;
+  a.max_context_len = pa_.max_context_len;
+  a.scale_log2 = pa_.scale * kLog2e;
+  a.q_aligned = ((uintptr_t)pa_.q & 15u) == 0 && pa_.q_st % 8 == 0 && pa_.q_sh % 8 == 0;
+  a.out_aligned = ((uintptr_t)pa_.out & 7u) == 0 && pa_.out_st % 4 == 0 && pa_.out_sh % 4 == 0;
+  a.q_heads = pa_.q_heads;
+  a.split_keys = pa_.split_keys;
+  a.max_chunks = pa_.max_chunks;
+  a.ws_o = pa_.ws_o;
+  a.ws_lse = pa_.ws_lse;
+  const int64_t grid = (int64_t)a.tiles_per_seq * a.max_chunks * pool.kv_heads * pa_.num_seqs;
+  prefill_kernel<D, G><<<(unsigned)grid, 256, 0, stream>>>(a);
+  if (a.max_chunks > 1)
+    prefill_merge_kernel<D><<<(unsigned)(pa_.total_tokens * pa_.q_heads), 64, 0, stream>>>(a);
 }
 
 template <int D>

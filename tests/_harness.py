@@ -86,7 +86,7 @@ class Setup:
         return pa.varlen_prefill(self.q, self.cu, self.pool, self.bt, self.ctx, c.scale,
                                  max_q_len=kw.pop("max_q_len", c.max_q_len),
                                  max_context_len=kw.pop("max_context_len", c.max_context_len),
-                                 **kw)
+                                 split_tokens=kw.pop("split_tokens", self.split_tokens), **kw)
 
     def oracle(self, seqs=None):
         c = self.case

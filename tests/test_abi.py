@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared()
     assert set(names) >= {"pa_store_kv", "pa_decode", "pa_varlen_prefill",
                           "pa_decode_workspace_bytes", "pa_status_string",
-                          "pa_decode_default_split_tokens"}
+                          "pa_decode_default_split_tokens", "pa_varlen_prefill_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in pa.SIGNATURES, f"binding lacks {n}"
@@ -93,6 +93,11 @@ def test_decode_validation(lib):
     assert decode(lib, p, maxctx=0) == INVALID
     assert decode(lib, p, split=8) == INVALID                # not a multiple of 16
     assert decode(lib, p, split=2048) == INVALID             # beyond 1024
+    assert lib.pa_decode(0x8000, 1536, 128, 0x9000, 1536, 128, pa.PA_BF16, 2, 12,
+                         ctypes.byref(p), 0xA000, 8, 0xB000, 128, -0.5, 0, 0, 0, None) == INVALID
+    assert lib.pa_decode(0x8000, 1536, 128, 0x9000, 1536, 128, pa.PA_BF16, 2, 12,
+                         ctypes.byref(p), 0xA000, 8, 0xB000, 128, float("nan"), 0, 0, 0,
+                         None) == INVALID
     # split 16 over up to 128 tokens needs a workspace
     assert decode(lib, p, split=16, ws=0) == WORKSPACE
     need = lib.pa_decode_workspace_bytes(2, 12, 2, 128, 128, 16)
@@ -118,9 +123,10 @@ def test_default_split_and_workspace_bytes(lib):
 
 
 def prefill(lib, pool, q_dtype=pa.PA_BF16, B=2, T=10, maxq=8, Hq=12, maxb=8, maxctx=128,
-            cu=0xD000):
+            cu=0xD000, split=0, ws=0, wsb=0):
     return lib.pa_varlen_prefill(0x8000, 1536, 128, 0x9000, 1536, 128, q_dtype, cu, B, T, maxq,
-                                 Hq, ctypes.byref(pool), 0xA000, maxb, 0xB000, maxctx, 0.1, None)
+                                 Hq, ctypes.byref(pool), 0xA000, maxb, 0xB000, maxctx, 0.1,
+                                 split, ws, wsb, None)
 
 
 def test_prefill_validation(lib):
@@ -133,3 +139,10 @@ def test_prefill_validation(lib):
     assert prefill(lib, p, maxq=200) == INVALID              # longer than any context
     assert prefill(lib, p, Hq=18) == UNSUPPORTED
     assert prefill(lib, fake_pool(pa.PA_F32), q_dtype=pa.PA_F32) == UNSUPPORTED
+    assert prefill(lib, p, split=32) == INVALID               # not a multiple of 64
+    assert prefill(lib, p, split=64, ws=0) == WORKSPACE       # 128 keys in 2 chunks
+    need = lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 128, 64)
+    assert need == 10 * 12 * 2 * 129 * 4
+    assert prefill(lib, p, split=64, ws=0xE000, wsb=need - 4) == WORKSPACE
+    assert lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 1024, 0) == 0
+    assert lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 1025, 0) == 10 * 12 * 2 * 129 * 4

@@ -12,18 +12,20 @@ from _harness import TOL, Setup, max_err
 pytestmark = pytest.mark.gpu
 
 
-def check(setup, tol=None):
-    out = setup.gpu()
+def check(setup, tol=None, **kw):
+    out = setup.gpu(**kw)
     torch.cuda.synchronize()
     err = max_err(out, setup.oracle())
     tol = tol or TOL[setup.case.kv_dtype]
-    print(f"{setup.case.name} max_abs_err={err:.3e} tol={tol}", flush=True)
+    print(f"{setup.case.name} kw={kw} max_abs_err={err:.3e} tol={tol}", flush=True)
     assert err <= tol
     return out
 
 
 def test_varlen_mixed_config(dev):
-    check(Setup(W.make(3), dev, poison=False))
+    s = Setup(W.make(3), dev, poison=False)
+    for split in (0, 64, 512, 4096):
+        check(s, split_tokens=split)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -32,7 +34,9 @@ def test_random_shapes(dev, D, G):
     hkv = 2 if G <= 4 else 1
     case = W.random_case(300 + G * 10 + D, kind="varlen", B=6, Hq=G * hkv, Hkv=hkv, D=D,
                          lmin=1, lmax=400, nmax=150)
-    check(Setup(case, dev))
+    s = Setup(case, dev)
+    check(s)
+    check(s, split_tokens=64)      # every tile past 64 visible keys is split and merged
 
 
 def test_zero_query_gives_causal_prefix_mean(dev):
@@ -58,7 +62,7 @@ def test_sequences_do_not_attend_across_boundaries(dev):
     case = W.random_case(22, kind="varlen", B=4, Hq=12, Hkv=2, D=128, lmin=20, lmax=300,
                          nmax=60)
     s = Setup(case, dev)
-    out = s.gpu()
+    outs = {split: s.gpu(split_tokens=split) for split in (0, 64)}
     # perturb sequence 1's queries and every slot of its blocks
     a, e = int(case.cu_seqlens[1]), int(case.cu_seqlens[2])
     q2 = s.q.clone()
@@ -67,11 +71,14 @@ def test_sequences_do_not_attend_across_boundaries(dev):
         if blk >= 0:
             s.pool.k[int(blk)] += 2.0
             s.pool.v[int(blk)] -= 3.0
-    out2 = pa.varlen_prefill(q2, s.cu, s.pool, s.bt, s.ctx, case.scale,
-                             max_q_len=case.max_q_len, max_context_len=case.max_context_len)
-    keep = torch.ones(out.shape[0], dtype=torch.bool)
+    keep = torch.ones(s.q.shape[0], dtype=torch.bool)
     keep[a:e] = False
-    assert torch.equal(out[keep.to(dev)], out2[keep.to(dev)])
+    keep = keep.to(dev)
+    for split, out in outs.items():
+        out2 = pa.varlen_prefill(q2, s.cu, s.pool, s.bt, s.ctx, case.scale,
+                                 max_q_len=case.max_q_len, max_context_len=case.max_context_len,
+                                 split_tokens=split)
+        assert torch.equal(out[keep], out2[keep])
 
 
 def test_decode_equals_varlen_with_chunks_of_one(dev):
@@ -89,16 +96,17 @@ def test_block_permutation_is_bit_identical(dev):
     case = W.random_case(24, kind="varlen", B=5, Hq=8, Hkv=2, D=128, lmin=5, lmax=500,
                          nmax=200)
     s = Setup(case, dev)
-    out = s.gpu()
     perm = np.random.default_rng(2).permutation(case.num_blocks)
     inv = np.argsort(perm)
     bt2 = np.where(case.block_tables >= 0, inv[np.maximum(case.block_tables, 0)], -1)
     p = torch.from_numpy(perm).to(dev)
     pool2 = pa.KVPool(s.pool.k[p].contiguous(), s.pool.v[p].contiguous())
-    out2 = pa.varlen_prefill(s.q, s.cu, pool2, torch.from_numpy(bt2.astype(np.int32)).to(dev),
-                             s.ctx, case.scale, max_q_len=case.max_q_len,
-                             max_context_len=case.max_context_len)
-    assert torch.equal(out, out2)
+    for split in (0, 128):
+        out = s.gpu(split_tokens=split)
+        out2 = pa.varlen_prefill(s.q, s.cu, pool2, torch.from_numpy(bt2.astype(np.int32)).to(dev),
+                                 s.ctx, case.scale, max_q_len=case.max_q_len,
+                                 max_context_len=case.max_context_len, split_tokens=split)
+        assert torch.equal(out, out2)
 
 
 def test_empty_chunks_and_strided_q(dev):
@@ -111,3 +119,33 @@ def test_empty_chunks_and_strided_q(dev):
                             max_q_len=max(1, case.max_q_len),
                             max_context_len=case.max_context_len)
     assert max_err(out, s.oracle()) <= TOL["bf16"]
+
+
+def test_chunked_prefill_equals_one_shot(dev):
+    """Prefill of n tokens in one call == the same tokens in two chunks (first chunk,
+    then the rest on top of it as cached prefix): chunked prefill on a cached prefix."""
+    case = W.random_case(26, kind="varlen", B=3, Hq=12, Hkv=2, D=128, lmin=200, lmax=600,
+                         nmax=180)
+    s = Setup(case, dev)
+    whole = s.gpu()
+    n = np.diff(case.cu_seqlens)
+    n1 = n // 2
+    n2 = n - n1
+    rows1 = np.concatenate([case.cu_seqlens[b] + np.arange(n1[b]) for b in range(3)])
+    rows2 = np.concatenate([case.cu_seqlens[b] + n1[b] + np.arange(n2[b]) for b in range(3)])
+    L2 = case.context_lens
+    L1 = (L2 - n2).astype(np.int32)
+    cu1 = np.concatenate([[0], np.cumsum(n1)]).astype(np.int32)
+    cu2 = np.concatenate([[0], np.cumsum(n2)]).astype(np.int32)
+    r1 = torch.from_numpy(rows1).to(dev)
+    r2 = torch.from_numpy(rows2).to(dev)
+    o1 = pa.varlen_prefill(s.q[r1].contiguous(), torch.from_numpy(cu1).to(dev), s.pool, s.bt,
+                           torch.from_numpy(L1).to(dev), case.scale,
+                           max_q_len=int(n1.max()), max_context_len=case.max_context_len)
+    o2 = pa.varlen_prefill(s.q[r2].contiguous(), torch.from_numpy(cu2).to(dev), s.pool, s.bt,
+                           torch.from_numpy(L2).to(dev), case.scale,
+                           max_q_len=int(n2.max()), max_context_len=case.max_context_len)
+    exp = s.oracle()
+    assert max_err(o1, exp[rows1]) <= TOL["bf16"]
+    assert max_err(o2, exp[rows2]) <= TOL["bf16"]
+    assert torch.max(torch.abs(o1.float() - whole[r1].float())).item() <= 2 * TOL["bf16"]
