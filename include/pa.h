@@ -137,9 +137,9 @@ int pa_store_kv(const pa_kv_pool_t *pool, const void *k, const void *v, int32_t 
 /*
  * pa_decode_workspace_bytes - bytes of device workspace pa_decode needs for these
  * sizes and this split length (0 when no context can need more than one split):
- * num_seqs*q_heads*max_splits*(head_dim+1) fp32 partials, with
- * max_splits = ceil(max_context_len / split). Returns 0 for invalid arguments as
- * well; pa_decode then reports the error.
+ * 4096 bytes of arrival counters, then num_seqs*q_heads*max_splits*(head_dim+1) fp32
+ * partials, with max_splits = ceil(max_context_len / split). Returns 0 for invalid
+ * arguments as well; pa_decode then reports the error.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
@@ -168,7 +168,8 @@ int32_t pa_decode_default_split_tokens(int32_t num_seqs, int32_t kv_heads,
  *   q            [num_seqs, q_heads, head_dim] of q_dtype, strides (q_stride_tok,
  *                q_stride_head) (a [B, 1, Hq, D] view works unchanged).
  *   block_tables [num_seqs, max_blocks_per_seq] int32, row-major. Entries past
- *                ceil(L / block_size) are never read.
+ *                ceil(L / block_size) may be loaded but are never used to address
+ *                the pool, so they may hold any value.
  *   context_lens [num_seqs] int32, each in [1, max_context_len].
  *   max_context_len  host-side upper bound of context_lens (sizes the grid).
  *   scale        softmax scale, finite and > 0 (e.g. 1/sqrt(head_dim)).
@@ -178,12 +179,20 @@ int32_t pa_decode_default_split_tokens(int32_t num_seqs, int32_t kv_heads,
  *                sequence s depends only on context_lens[s], so its output bits do
  *                not depend on the rest of the batch; pass an explicit value to keep
  *                that when batch shapes vary.
- *   workspace    device scratch of at least pa_decode_workspace_bytes(...) bytes for
- *                the same (num_seqs, q_heads, kv_heads, head_dim, max_context_len,
- *                split_tokens);
- *                may be NULL when that is 0. It holds the per-split partials (o, lse),
- *                is fully overwritten before it is read, so its contents on entry are
- *                ignored. Two calls in flight must not share a workspace.
+ *   workspace    16-byte aligned device scratch of at least pa_decode_workspace_bytes(...)
+ *                bytes for the same (num_seqs, q_heads, kv_heads, head_dim,
+ *                max_context_len, split_tokens); may be NULL when that is 0. It holds
+ *                arrival counters in its first 4096 bytes, which MUST be zero before
+ *                the first call (zero-fill the workspace once when allocating it), and
+ *                the split partials (o, lse) after them, written before they are read.
+ *                Every call leaves the counters zero and writes no partial into them,
+ *                so a workspace can be reused by any later call whose size fits.
+ *                Two calls in flight must not share a workspace.
+ * Split partials are merged by log-sum-exp in two levels, both in index order: each
+ * group of 8 consecutive splits, then the groups. Small calls (at most 1024
+ * (sequence, group, KV head) triples) run as one launch in which the last group of a
+ * sequence to finish merges the others; larger ones as a persistent split launch plus
+ * a merge launch. Both give identical bits.
  * Accumulation is fp32; out is rounded once (round-to-nearest-even) to q_dtype.
  */
 int pa_decode(void *out, int64_t out_stride_tok, int64_t out_stride_head, const void *q,
@@ -215,7 +224,7 @@ int pa_decode(void *out, int64_t out_stride_tok, int64_t out_stride_head, const 
  *                tile whose visible keys exceed it is split into key chunks handled
  *                in parallel and merged by log-sum-exp; results depend bitwise only
  *                on this value and each sequence's own (n_s, context_lens[s]).
- *   workspace    device scratch of at least pa_varlen_prefill_workspace_bytes(...)
+ *   workspace    16-byte aligned device scratch of at least pa_varlen_prefill_workspace_bytes(...)
  *                bytes for the same (total_tokens, q_heads, head_dim, max_context_len,
  *                split_tokens); may be NULL when that is 0; contents on entry ignored.
  *   Other arguments as in pa_decode. A chunk of length 1 is a decode row.

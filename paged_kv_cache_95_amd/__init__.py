@@ -174,10 +174,11 @@ def decode_workspace_bytes(num_seqs, q_heads, kv_heads, head_dim, max_context_le
 
 def decode_workspace(num_seqs, q_heads, kv_heads, head_dim, max_context_len, split_tokens=0,
                      device="cuda"):
-    """A workspace for decode() calls of these sizes (and split length)."""
+    """A workspace for decode() calls of these sizes (and split length), zero-filled as
+    pa_decode requires before first use (its arrival counters); calls leave it reusable."""
     need = decode_workspace_bytes(num_seqs, q_heads, kv_heads, head_dim, max_context_len,
                                   split_tokens)
-    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
 
 
 def _meta(block_tables, context_lens):
@@ -202,7 +203,7 @@ def decode(q, pool, block_tables, context_lens, scale, max_context_len=None, spl
     qs, os_ = _rows3(q, "q"), _rows3(out, "out")
     need = decode_workspace_bytes(B, Hq, pool.kv_heads, D, max_context_len, split_tokens)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pa_decode(_ptr(out), os_[0], os_[1], _ptr(q), qs[0], qs[1], _DTYPE_CODE[q.dtype],
                            B, Hq, pool.struct, _ptr(block_tables), block_tables.shape[1],

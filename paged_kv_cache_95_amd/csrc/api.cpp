@@ -4,6 +4,8 @@
 // launches nothing (and can be exercised without a GPU). No exception crosses the ABI.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace {
@@ -70,6 +72,7 @@ int32_t pa_decode_default_split_tokens(int32_t num_seqs, int32_t kv_heads,
   return effective_split(0, num_seqs, kv_heads, max_context_len);
 }
 
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t split_tokens) {
@@ -79,7 +82,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t kv_h
   const int split = effective_split(split_tokens, num_seqs, kv_heads, max_context_len);
   const int64_t max_splits = ((int64_t)max_context_len + split - 1) / split;
   if (max_splits <= 1) return 0;
-  return (size_t)num_seqs * q_heads * max_splits * (head_dim + 1) * sizeof(float);
+  return pa::kDecodeCounterBytes +
+         (size_t)num_seqs * q_heads * max_splits * (head_dim + 1) * sizeof(float);
 }
 
 int pa_store_kv(const pa_kv_pool_t* pool, const void* k, const void* v, int32_t src_dtype,
@@ -127,7 +131,8 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
   const int max_splits = (max_context_len + split - 1) / split;
   const size_t need = pa_decode_workspace_bytes(num_seqs, q_heads, pool->kv_heads,
                                                 pool->head_dim, max_context_len, split);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u) != 0))
+    return PA_ERR_WORKSPACE;
   const int64_t grid = ((int64_t)num_seqs * max_splits * pool->kv_heads + 3) / 4;
   if (grid >= (int64_t)1 << 31 || (int64_t)num_seqs * q_heads >= (int64_t)1 << 31)
     return PA_ERR_UNSUPPORTED;
@@ -148,7 +153,9 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
   a.scale = scale;
   a.split_tokens = split;
   a.max_splits = max_splits;
-  a.ws_o = (float*)workspace;  // [num_seqs, q_heads, max_splits, head_dim], then lse
+  // workspace: [arrival counters, fixed 4 KiB][o: num_seqs, q_heads, max_splits, D][lse]
+  a.counters = need > 0 ? (unsigned*)workspace : nullptr;
+  a.ws_o = need > 0 ? (float*)((char*)workspace + pa::kDecodeCounterBytes) : nullptr;
   a.ws_lse = need > 0 ? a.ws_o + (size_t)num_seqs * q_heads * max_splits * pool->head_dim
                       : nullptr;
   return launched(pa::launch_decode(*pool, a, (hipStream_t)stream));
@@ -195,9 +202,11 @@ int pa_varlen_prefill(void* out, int64_t out_stride_tok, int64_t out_stride_head
   const int max_chunks = (max_context_len + split - 1) / split;
   const size_t need = pa_varlen_prefill_workspace_bytes(total_tokens, q_heads, pool->head_dim,
                                                         max_context_len, split);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u) != 0))
+    return PA_ERR_WORKSPACE;
   const int64_t tiles = ((int64_t)max_q_len * (q_heads / pool->kv_heads) + 127) / 128;
-  if (tiles * max_chunks * pool->kv_heads * num_seqs >= (int64_t)1 << 31 ||
+  // prefill grid, and the merge grid (at most 4 workgroups per row tile)
+  if (tiles * std::max(max_chunks, 4) * pool->kv_heads * num_seqs >= (int64_t)1 << 31 ||
       total_tokens * q_heads >= (int64_t)1 << 31)
     return PA_ERR_UNSUPPORTED;
 

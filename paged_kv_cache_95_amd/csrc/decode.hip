@@ -241,8 +241,10 @@ struct SplitArgs {
   float scale_log2;
   int split_tokens;
   int max_splits;
-  float* ws_o;
-  float* ws_lse;
+  float* ws_o;       // [num_seqs, q_heads, max_splits, D] split (or group) partials
+  float* ws_lse;     // [num_seqs, q_heads, max_splits]
+  int max_chunks;    // ceil(max_splits / kGroupSplits): groups per sequence, at most
+  unsigned* counters;  // [num_seqs, kv_heads] arrival counters, zero between calls
   bool q_aligned;    // q rows start on 16-byte boundaries (base and strides)
   bool out_aligned;  // same for out
 };
@@ -257,37 +259,30 @@ __device__ __forceinline__ int num_splits(int L, int split_tokens) {
   return L > 0 ? (L + split_tokens - 1) / split_tokens : 0;
 }
 
-// One work item (sequence s, split, kv head g) on one wavefront.
+// Inputs of one work item that do not depend on its context length: the G query rows
+// (as this lane's dot-product operands) and the block ids of the split (lane j holds
+// entry jb0 + j; a split is at most 64 blocks). Issuing these before the length is
+// known takes one dependent memory round trip off each item. Table entries past the
+// context are loaded but never used for addressing.
+template <int KVT, int D, int G>
+struct ItemIn {
+  uint32_t qw[G][Geom<KVT, D>::QW];
+  int bid_lane;
+};
+
 template <int KVT, int D, int G, int QT>
-__device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split, int g, int L,
-                                            int nsplit, int lane) {
+__device__ __forceinline__ void load_item_inputs(const SplitArgs& a, int s, int split, int g,
+                                                 int lane, ItemIn<KVT, D, G>& in) {
   using Gm = Geom<KVT, D>;
-  constexpr float NEG_INF = -__builtin_huge_valf();
-  const int t0 = split * a.split_tokens;
-  const int t1 = min(L, t0 + a.split_tokens);
-  const int jb0 = t0 / kBlockSize;
-  const int nblk = (t1 - t0 + kBlockSize - 1) / kBlockSize;
-
-  // ---- block ids of this split: lane j holds entry jb0 + j (a split is <= 64 blocks)
+  const int jb0 = split * (a.split_tokens / kBlockSize);
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int bid_lane = lane < nblk ? bt_row[jb0 + lane] : 0;
-
-  // ---- lane geometry
-  const int r = lane >> 4;
-  const int half = (lane >> 3) & 1;
+  in.bid_lane = (lane < a.split_tokens / kBlockSize && jb0 + lane < a.max_blocks_per_seq)
+                    ? bt_row[jb0 + lane]
+                    : 0;
   const int t8 = lane & 7;
-  const int cv = lane & 15;
   const bool k_lane = t8 < Gm::NCH;  // false only for rows shorter than 8 chunks
-  int tok_k[2], tok_v[4];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    tok_k[k] = 8 * k + 2 * r + half;
-    tok_v[2 * k] = tok_k[k];
-    tok_v[2 * k + 1] = 8 * k + 2 * r + (half ^ 1);
-  }
-
+  uint32_t (&qw)[G][Gm::QW] = in.qw;
   // ---- query chunks t8 + 8j of the G heads (bf16 pairs, or fp32)
-  uint32_t qw[G][Gm::QW];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const int64_t qoff = (int64_t)s * a.q_st + (int64_t)(g * G + h) * a.q_sh;
@@ -322,6 +317,39 @@ __device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split
               k_lane ? ((uint32_t)qp[2 * e] | ((uint32_t)qp[2 * e + 1] << 16)) : 0u;
       }
     }
+  }
+
+}
+
+// One work item (sequence s, split, kv head g) on one wavefront: the split's partial
+// attention for the G heads of group g, normalised (o = sum p v / sum p) with its
+// log2-sum-exp, in lanes 0..15 (lane c holds head dims [c*D/16, (c+1)*D/16)). A split
+// past the context (possible in the fused schedule) yields lse2 = -inf.
+template <int KVT, int D, int G>
+__device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KVT, D, G>& in,
+                                             int split, int g, int L, int lane,
+                                             float (&o)[G][Geom<KVT, D>::EV], float (&lse2)[G]) {
+  using Gm = Geom<KVT, D>;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  const int t0 = split * a.split_tokens;
+  const int t1 = min(L, t0 + a.split_tokens);
+  const int jb0 = t0 / kBlockSize;
+  const int nblk = t1 > t0 ? (t1 - t0 + kBlockSize - 1) / kBlockSize : 0;
+  const int bid_lane = in.bid_lane;
+  const uint32_t (&qw)[G][Gm::QW] = in.qw;
+
+  // ---- lane geometry
+  const int r = lane >> 4;
+  const int half = (lane >> 3) & 1;
+  const int t8 = lane & 7;
+  const int cv = lane & 15;
+  const bool k_lane = t8 < Gm::NCH;  // false only for rows shorter than 8 chunks
+  int tok_k[2], tok_v[4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    tok_k[k] = 8 * k + 2 * r + half;
+    tok_v[2 * k] = tok_k[k];
+    tok_v[2 * k + 1] = 8 * k + 2 * r + (half ^ 1);
   }
 
   const int64_t blk_bytes = (int64_t)kBlockSize * a.hkv * Gm::ROW;
@@ -397,7 +425,7 @@ __device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split
   }
 
   // ---- combine the four DPP rows: per head, rescale to the wave max and sum
-  float inv_l[G], lse2[G];
+  float inv_l[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float M = fmaxf(st.m[h], __shfl_xor(st.m[h], 16));
@@ -415,23 +443,39 @@ __device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split
     }
     inv_l[h] = 1.0f / lr;
     lse2[h] = M + __log2f(lr);
+#pragma unroll
+    for (int e = 0; e < Gm::EV; ++e) o[h][e] = st.acc[h][e] * inv_l[h];
   }
+}
+
+// Result of one item in the split-then-merge schedule: the final output row when the
+// sequence has a single split, else the partial in the workspace.
+template <int KVT, int D, int G, int QT>
+__device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split, int g,
+                                            int lane) {
+  using Gm = Geom<KVT, D>;
+  ItemIn<KVT, D, G> in;
+  load_item_inputs<KVT, D, G, QT>(a, s, split, g, lane, in);
+  const int L = clamped_len(a, s);
+  const int nsplit = num_splits(L, a.split_tokens);
+  float o[G][Gm::EV], lse2[G];
+  item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2);
   if (lane >= 16) return;
+  const int cv = lane;
   const int d0 = cv * Gm::EV;
   if (nsplit == 1) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const int64_t o = (int64_t)s * a.out_st + (int64_t)(g * G + h) * a.out_sh + d0;
+      const int64_t off = (int64_t)s * a.out_st + (int64_t)(g * G + h) * a.out_sh + d0;
       if constexpr (QT == kF32) {
 #pragma unroll
-        for (int e = 0; e < Gm::EV; ++e) ((float*)a.out)[o + e] = st.acc[h][e] * inv_l[h];
+        for (int e = 0; e < Gm::EV; ++e) ((float*)a.out)[off + e] = o[h][e];
       } else {
         uint32_t w[Gm::EV / 2];
 #pragma unroll
         for (int e = 0; e < Gm::EV / 2; ++e)
-          w[e] = (uint32_t)f32_to_bf16(st.acc[h][2 * e] * inv_l[h]) |
-                 ((uint32_t)f32_to_bf16(st.acc[h][2 * e + 1] * inv_l[h]) << 16);
-        uint16_t* op = (uint16_t*)a.out + o;
+          w[e] = (uint32_t)f32_to_bf16(o[h][2 * e]) | ((uint32_t)f32_to_bf16(o[h][2 * e + 1]) << 16);
+        uint16_t* op = (uint16_t*)a.out + off;
         if (a.out_aligned && Gm::EV == 8) {
           *reinterpret_cast<uint4*>(op) = make_uint4(w[0], w[1], w[2], w[3]);
         } else {
@@ -451,7 +495,7 @@ __device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split
     const int64_t row = ((int64_t)s * hq + g * G + h) * a.max_splits + split;
     float* wo = a.ws_o + row * D + d0;
 #pragma unroll
-    for (int e = 0; e < Gm::EV; ++e) wo[e] = st.acc[h][e] * inv_l[h];
+    for (int e = 0; e < Gm::EV; ++e) wo[e] = o[h][e];
     if (cv == 0) a.ws_lse[row] = lse2[h];
   }
 }
@@ -471,7 +515,7 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(SplitArgs a) 
   const int L = clamped_len(a, s);
   const int nsplit = num_splits(L, a.split_tokens);
   if (split >= nsplit) return;
-  decode_item<KVT, D, G, QT>(a, s, split, g, L, nsplit, lane);
+  decode_item<KVT, D, G, QT>(a, s, split, g, lane);
 }
 
 // Compact persistent schedule. Every workgroup prefix-sums the per-sequence split
@@ -539,103 +583,255 @@ __global__ void __launch_bounds__(64 * kWaves) decode_compact_kernel(SplitArgs a
       s = lo;
     }
     while (cum[s + 1] <= pair) ++s;
-    const int L = clamped_len(a, s);
-    decode_item<KVT, D, G, QT>(a, s, pair - cum[s], g, L, num_splits(L, a.split_tokens), lane);
+    decode_item<KVT, D, G, QT>(a, s, pair - cum[s], g, lane);
   }
 }
 
-// Log-sum-exp merge of the split partials of one (sequence, query head) per 256-thread
-// workgroup: out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M), M = max_i lse_i. A
-// separate launch orders it after every split (a device-scope fence in each split
-// wave instead would write back and invalidate the L2 once per wave).
-// Thread = 16 * grp + c: c owns head dims [c*D/16, (c+1)*D/16), grp (0..15) takes
-// splits grp, grp+16, ...; loads of four such splits are issued together and kept
-// as a running (max, sum, acc), then the 16 groups are combined (shuffles, then LDS).
+// ---------------------------------------------------------------- log-sum-exp merge
+// Partials are merged in two levels, in index order: the splits of each group of
+// kGroupSplits consecutive splits first, then the groups. Both schedules below follow
+// exactly this order with the same float operations, so a sequence's output bits
+// depend only on its own length and split_tokens, whichever schedule runs.
+//   level 1 (group c):  M = max lse_i, den = sum 2^(lse_i - M), acc = sum 2^(lse_i - M) o_i
+//                       (online, i ascending, splits with lse = -inf skipped);
+//                       group partial o_c = acc * (1/den), lse_c = M + log2(den)
+//   level 2:            the same online merge over the groups, out = acc * (1/den).
+// A sequence with a single group writes level 1's acc * (1/den) directly.
+constexpr int kGroupSplits = 8;
+// Calls with at most this many (sequence, group, KV head) workgroups take the single-
+// launch schedule; larger ones the persistent split kernel plus a merge launch.
+constexpr int64_t kFusedMaxWorkgroups = 1024;
+
+struct Merge4 {
+  float m, den, acc[4];
+  __device__ __forceinline__ void init() {
+    m = -__builtin_huge_valf();
+    den = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = 0.0f;
+  }
+  // Branch-free so that a run of adds can consume operands loaded ahead of it; a
+  // split or group with no token (lse = -inf, o undefined) leaves the state as is.
+  __device__ __forceinline__ void add(float lse, const float4& o) {
+    const bool ok = lse != -__builtin_huge_valf();
+    const float m_new = ok ? fmaxf(m, lse) : m;
+    const float f = ok ? fast_exp2(m - m_new) : 1.0f;  // 0 while m is -inf
+    const float w = ok ? fast_exp2(lse - m_new) : 0.0f;
+    den = ok ? fmaf(den, f, w) : den;
+    acc[0] = ok ? fmaf(acc[0], f, w * o.x) : acc[0];
+    acc[1] = ok ? fmaf(acc[1], f, w * o.y) : acc[1];
+    acc[2] = ok ? fmaf(acc[2], f, w * o.z) : acc[2];
+    acc[3] = ok ? fmaf(acc[3], f, w * o.w) : acc[3];
+    m = m_new;
+  }
+};
+
+// Four consecutive output elements (d multiple of 4) of row (s, qh), scaled by inv.
+template <int QT>
+__device__ __forceinline__ void store_out4(void* out, int64_t out_st, int64_t out_sh,
+                                           bool out_aligned, int s, int qh, int d,
+                                           const float (&v)[4], float inv) {
+  const int64_t off = (int64_t)s * out_st + (int64_t)qh * out_sh + d;
+  if constexpr (QT == kF32) {
+    float* op = (float*)out + off;
+    if (out_aligned) {
+      *reinterpret_cast<float4*>(op) = make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) op[e] = v[e] * inv;
+    }
+  } else {
+    const uint32_t w0 = (uint32_t)f32_to_bf16(v[0] * inv) | ((uint32_t)f32_to_bf16(v[1] * inv) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16(v[2] * inv) | ((uint32_t)f32_to_bf16(v[3] * inv) << 16);
+    uint16_t* op = (uint16_t*)out + off;
+    if (out_aligned) {
+      *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
+    } else {
+      op[0] = (uint16_t)w0;
+      op[1] = (uint16_t)(w0 >> 16);
+      op[2] = (uint16_t)w1;
+      op[3] = (uint16_t)(w1 >> 16);
+    }
+  }
+}
+
+// Device-coherent (agent-scope, relaxed) accesses for the single-launch schedule's
+// cross-workgroup exchange. On gfx950 these are plain vector loads and stores with the
+// device-scope cache policy, which bypasses the non-coherent per-XCD L2 state, so no
+// L2 writeback or invalidate is needed; ordering comes from waiting for the stores to
+// complete before the arrival counter is incremented.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Level 2 over the group partials 0..ngroups-1 of row0 (group stride = partial rows),
+// read with device-coherent loads, sixteen groups' loads issued together.
+template <int D>
+__device__ __forceinline__ void merge_groups_coherent(const float* ws_o, const float* ws_lse,
+                                                      int64_t row0, int ngroups, int d,
+                                                      Merge4& mg) {
+  constexpr int U = 16;
+  for (int c0 = 0; c0 < ngroups; c0 += U) {
+    float lse[U];
+    float4 o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u;
+      lse[u] = -__builtin_huge_valf();
+      o[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (c < ngroups) {  // uniform: no load is spent on a missing group
+        const int64_t row = row0 + c;
+        const float* op = ws_o + row * D + d;
+        lse[u] = ld_dev(ws_lse + row);
+        o[u] = make_float4(ld_dev(op), ld_dev(op + 1), ld_dev(op + 2), ld_dev(op + 3));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) mg.add(lse[u], o[u]);
+  }
+}
+
+// Merge launch of the split-then-merge schedule: one workgroup per (sequence, KV head);
+// thread t owns column (head h = t / (D/4), dims 4*(t % (D/4)) .. +3) of the G query
+// heads, runs level 1 over each group's split partials and folds each group result
+// into level 2 as it goes.
 constexpr int kMergeThreads = 256;
 
-template <int D, int QT>
-__global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(
-    void* __restrict__ out, int64_t out_st, int64_t out_sh, int q_heads,
-    const int32_t* __restrict__ context_lens, int max_context_len, int split_tokens,
-    int max_splits, const float* __restrict__ ws_o, const float* __restrict__ ws_lse) {
-  constexpr int EV = D / 16;
-  constexpr int GROUPS = kMergeThreads / 16;
-  constexpr float NEG_INF = -__builtin_huge_valf();
-  constexpr int UNROLL = 4;
-  const int h = blockIdx.x % q_heads;
-  const int s = blockIdx.x / q_heads;
-  const int L = min(context_lens[s], max_context_len);
-  const int nsplit = L > 0 ? (L + split_tokens - 1) / split_tokens : 0;
-  if (nsplit <= 1) return;  // written directly by the split kernel (uniform exit)
-  const int tid = threadIdx.x;
-  const int grp = tid >> 4;
-  const int c = tid & 15;
-  const int64_t row0 = ((int64_t)s * q_heads + h) * max_splits;
-  float m = NEG_INF, den = 0.0f, acc[EV];
+template <int D, int G, int QT>
+__global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(SplitArgs a) {
+  constexpr int D4 = D / 4;
+  const int g = (int)(blockIdx.x % a.hkv);
+  const int s = (int)(blockIdx.x / a.hkv);
+  const int L = clamped_len(a, s);
+  const int nsplit = num_splits(L, a.split_tokens);
+  if (nsplit <= 1) return;  // written directly by the split kernel
+  const int t = threadIdx.x;
+  if (t >= G * D4) return;
+  const int h = t / D4, d = 4 * (t % D4);
+  const int qh = g * G + h;
+  const int64_t row0 = ((int64_t)s * a.hkv * G + qh) * a.max_splits;
+  const int ngroups = (nsplit + kGroupSplits - 1) / kGroupSplits;
+  Merge4 top;
+  top.init();
+  for (int c = 0; c < ngroups; ++c) {
+    // level 1 over the (at most kGroupSplits) splits of group c
+    const int i0 = c * kGroupSplits;
+    const int n = min(kGroupSplits, nsplit - i0);
+    float lse[kGroupSplits];
+    float4 o[kGroupSplits];
 #pragma unroll
-  for (int e = 0; e < EV; ++e) acc[e] = 0.0f;
-  for (int i0 = grp; i0 < nsplit; i0 += GROUPS * UNROLL) {
-    float lse[UNROLL];
-    float o[UNROLL][EV];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int i = i0 + GROUPS * u;
-      const bool ok = i < nsplit;
-      lse[u] = ok ? ws_lse[row0 + i] : NEG_INF;
-      const float* op = ws_o + (row0 + (ok ? i : i0)) * D + c * EV;
-#pragma unroll
-      for (int e = 0; e < EV; ++e) o[u][e] = op[e];
+    for (int u = 0; u < kGroupSplits; ++u) {
+      const int64_t row = row0 + i0 + (u < n ? u : 0);
+      lse[u] = u < n ? a.ws_lse[row] : -__builtin_huge_valf();
+      o[u] = *reinterpret_cast<const float4*>(a.ws_o + row * D + d);
     }
+    Merge4 grp;
+    grp.init();
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      if (lse[u] == NEG_INF) continue;
-      const float m_new = fmaxf(m, lse[u]);
-      const float a = fast_exp2(m - m_new);  // 0 while m is -inf
-      const float w = fast_exp2(lse[u] - m_new);
-      den = fmaf(den, a, w);
-#pragma unroll
-      for (int e = 0; e < EV; ++e) acc[e] = fmaf(acc[e], a, w * o[u][e]);
-      m = m_new;
+    for (int u = 0; u < kGroupSplits; ++u) grp.add(lse[u], o[u]);
+    if (ngroups == 1) {
+      store_out4<QT>(a.out, a.out_st, a.out_sh, a.out_aligned, s, qh, d, grp.acc, 1.0f / grp.den);
+      return;
     }
+    // level 2, online over the groups as they complete
+    const float inv = 1.0f / grp.den;
+    const float4 og = make_float4(grp.acc[0] * inv, grp.acc[1] * inv, grp.acc[2] * inv,
+                                  grp.acc[3] * inv);
+    top.add(grp.m + __log2f(grp.den), og);
   }
-  // combine groups: the four of a wave by shuffles, then the four waves through LDS
-  auto combine = [&](float m_o, float d_o, const float* a_o) {
-    const float m_new = fmaxf(m, m_o);
-    const float a = m == NEG_INF ? 0.0f : fast_exp2(m - m_new);
-    const float b = m_o == NEG_INF ? 0.0f : fast_exp2(m_o - m_new);
-    den = den * a + d_o * b;
+  store_out4<QT>(a.out, a.out_st, a.out_sh, a.out_aligned, s, qh, d, top.acc, 1.0f / top.den);
+}
+
+// Single-launch schedule for small batches (latency bound: a handful of sequences
+// whose whole KV fits in one pass of the GPU). One workgroup of kGroupSplits waves per
+// (sequence, group of kGroupSplits consecutive splits, KV head), on a plain grid: the
+// item's query rows and block ids are requested before its context length is known,
+// the waves' partials are merged in LDS (level 1), and a sequence with several groups
+// publishes group partials to the workspace and counts arrivals on a per (sequence,
+// KV head) counter; the last group to arrive merges them (level 2) and writes out,
+// then returns the counter to zero. This replaces the merge launch and its dependent
+// loads, which dominate the time of such small calls.
+template <int KVT, int D, int G, int QT>
+__global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitArgs a) {
+  using Gm = Geom<KVT, D>;
+  constexpr int NW = kGroupSplits;
+  constexpr int D4 = D / 4;
+  static_assert(G * D4 <= 64 * NW, "one merge column per thread");
+  __shared__ float part_o[NW][G][D];
+  __shared__ float part_lse[NW][G];
+  __shared__ unsigned arrival;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = (int)(blockIdx.x % a.hkv);
+  const int rest = (int)(blockIdx.x / a.hkv);
+  const int c = rest % a.max_chunks;
+  const int s = rest / a.max_chunks;
+  const int split = c * NW + wave;
+  ItemIn<KVT, D, G> in;
+  load_item_inputs<KVT, D, G, QT>(a, s, split, g, lane, in);
+  const int L = clamped_len(a, s);
+  const int nsplit = num_splits(L, a.split_tokens);
+  const int ngroups = (nsplit + NW - 1) / NW;
+  if (c >= ngroups) return;  // uniform over the workgroup, before any barrier
+  float o[G][Gm::EV], lse2[G];
+  item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2);
+  if (lane < 16) {
 #pragma unroll
-    for (int e = 0; e < EV; ++e) acc[e] = acc[e] * a + a_o[e] * b;
-    m = m_new;
-  };
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-    float a_o[EV];
+      for (int e = 0; e < Gm::EV; ++e) part_o[wave][h][lane * Gm::EV + e] = o[h][e];
+    if (lane == 0) {
 #pragma unroll
-    for (int e = 0; e < EV; ++e) a_o[e] = __shfl_xor(acc[e], off);
-    const float m_o = __shfl_xor(m, off);
-    const float d_o = __shfl_xor(den, off);
-    combine(m_o, d_o, a_o);
-  }
-  __shared__ float part[kMergeThreads / 64][16][EV + 2];
-  const int wave = tid >> 6;
-  if ((tid & 63) < 16) {
-    part[wave][c][0] = m;
-    part[wave][c][1] = den;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) part[wave][c][2 + e] = acc[e];
+      for (int h = 0; h < G; ++h) part_lse[wave][h] = lse2[h];
+    }
   }
   __syncthreads();
-  if (tid >= 16) return;
+  const int t = threadIdx.x;
+  const bool col = t < G * D4;
+  const int h = col ? t / D4 : 0, d = 4 * (t % D4);
+  const int qh = g * G + h;
+  Merge4 grp;
+  grp.init();
+  if (col) {
+    float lw[NW];
+    float4 ow[NW];
 #pragma unroll
-  for (int w = 1; w < kMergeThreads / 64; ++w) combine(part[w][c][0], part[w][c][1], &part[w][c][2]);
-  const float inv = 1.0f / den;
-  const int64_t base = (int64_t)s * out_st + (int64_t)h * out_sh + c * EV;
+    for (int w = 0; w < NW; ++w) {
+      lw[w] = part_lse[w][h];
+      ow[w] = *reinterpret_cast<const float4*>(&part_o[w][h][d]);
+    }
 #pragma unroll
-  for (int e = 0; e < EV; ++e) {
-    if constexpr (QT == kF32) ((float*)out)[base + e] = acc[e] * inv;
-    else ((uint16_t*)out)[base + e] = f32_to_bf16(acc[e] * inv);
+    for (int w = 0; w < NW; ++w) grp.add(lw[w], ow[w]);
   }
+  if (ngroups == 1) {
+    if (col) store_out4<QT>(a.out, a.out_st, a.out_sh, a.out_aligned, s, qh, d, grp.acc, 1.0f / grp.den);
+    return;
+  }
+  const int64_t row0 = ((int64_t)s * a.hkv * G + qh) * a.max_splits;
+  if (col) {
+    const float inv = 1.0f / grp.den;
+    float* wo = a.ws_o + (row0 + c) * D + d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st_dev(wo + e, grp.acc[e] * inv);
+    if (d == 0) st_dev(a.ws_lse + row0 + c, grp.m + __log2f(grp.den));
+  }
+  // every thread's partial stores have completed before the arrival is counted
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  unsigned* counter = a.counters + ((int64_t)s * a.hkv + g);
+  if (t == 0)
+    arrival = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (arrival != (unsigned)(ngroups - 1)) return;
+  if (col) {
+    Merge4 top;
+    top.init();
+    merge_groups_coherent<D>(a.ws_o, a.ws_lse, row0, ngroups, d, top);
+    store_out4<QT>(a.out, a.out_st, a.out_sh, a.out_aligned, s, qh, d, top.acc, 1.0f / top.den);
+  }
+  if (t == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Resident workgroups of a kernel on the whole device (CUs x workgroups per CU).
@@ -682,6 +878,14 @@ static void launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, hipSt
   };
   sa.q_aligned = al(a.q, a.q_st, a.q_sh, qe);
   sa.out_aligned = al(a.out, a.out_st, a.out_sh, qe);
+  sa.max_chunks = (a.max_splits + kGroupSplits - 1) / kGroupSplits;
+  sa.counters = a.counters;
+  const int64_t fused_groups = (int64_t)a.num_seqs * pool.kv_heads * sa.max_chunks;
+  static_assert(kFusedMaxWorkgroups <= kDecodeCounters, "one counter per (sequence, KV head)");
+  if (fused_groups <= kFusedMaxWorkgroups) {
+    decode_fused_kernel<KVT, D, G, QT><<<(unsigned)fused_groups, 64 * kGroupSplits, 0, stream>>>(sa);
+    return;
+  }
   const int64_t items = (int64_t)a.num_seqs * a.max_splits * pool.kv_heads;
   const int64_t steps = (items + kWaves - 1) / kWaves;  // upper bound of workgroup steps
   if (a.num_seqs <= kMaxCompactSeqs) {
@@ -692,10 +896,8 @@ static void launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, hipSt
     decode_split_kernel<KVT, D, G, QT><<<(unsigned)steps, 64 * kWaves, 0, stream>>>(sa);
   }
   if (a.max_splits > 1)
-    decode_merge_kernel<D, QT><<<(unsigned)((int64_t)a.num_seqs * a.q_heads), kMergeThreads, 0,
-                                 stream>>>(
-        a.out, a.out_st, a.out_sh, a.q_heads, a.context_lens, a.max_context_len,
-        a.split_tokens, a.max_splits, a.ws_o, a.ws_lse);
+    decode_merge_kernel<D, G, QT><<<(unsigned)((int64_t)a.num_seqs * pool.kv_heads),
+                                    kMergeThreads, 0, stream>>>(sa);
 }
 
 template <int KVT, int D, int QT>

@@ -29,7 +29,14 @@ struct DecodeArgs {
   int max_splits;
   float* ws_o;    // [num_seqs, q_heads, max_splits, head_dim]
   float* ws_lse;  // [num_seqs, q_heads, max_splits]
+  unsigned* counters;  // [num_seqs, kv_heads] used of kDecodeCounters, zero between calls
 };
+
+// The decode workspace starts with a fixed block of arrival counters (the single-launch
+// schedule uses one per (sequence, KV head) and runs only when there are at most this
+// many), so the same bytes are counters in every call and never hold partials.
+constexpr int kDecodeCounters = 1024;
+constexpr size_t kDecodeCounterBytes = kDecodeCounters * sizeof(unsigned);
 
 
 int launch_decode(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream);

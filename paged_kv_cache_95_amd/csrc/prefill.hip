@@ -369,54 +369,95 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PfArgs a) {
     }
 }
 
-// Merge of the key-chunk partials of one (token, query head) per wavefront, for tokens
-// whose row tile was split: out = sum_c 2^(lse_c - M) o_c / sum_c 2^(lse_c - M).
+// Merge of the key-chunk partials. The prefill grid's row tiles are cut into parts of
+// 256 / (D/16) rows; one 256-thread workgroup per (part, row tile, KV head, sequence),
+// one thread per (row, 16-float slice of head_dim), slice fastest so neighbouring
+// threads read neighbouring 64-byte pieces of a partial. Tiles with a single key chunk
+// were written directly by the prefill kernel and their workgroups exit after one load
+// of the sizes. Each thread runs an online log-sum-exp merge over the chunks, loading
+// four chunks ahead.
 template <int D>
-__global__ void __launch_bounds__(64) prefill_merge_kernel(PfArgs a) {
+constexpr int pf_merge_rows() { return 256 / (D / 16); }
+
+template <int D>
+__global__ void __launch_bounds__(256) prefill_merge_kernel(PfArgs a) {
+  constexpr int NS = D / 16;
+  constexpr int ROWS = pf_merge_rows<D>();
+  constexpr int PARTS = kPfRows / ROWS;
   constexpr float NEG_INF = -__builtin_huge_valf();
-  const int h = (int)(blockIdx.x % a.q_heads);
-  const int64_t t = blockIdx.x / a.q_heads;
+  const int part = (int)(blockIdx.x % PARTS);
+  const int mt = (int)((blockIdx.x / PARTS) % a.tiles_per_seq);
+  const int rest = (int)(blockIdx.x / PARTS / a.tiles_per_seq);
+  const int g = rest % a.hkv;
+  const int s = rest / a.hkv;
   const int G = a.q_heads / a.hkv;
-  // sequence of token t: the first s with cu[s + 1] > t
-  int lo = 0, hi = a.num_seqs;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a.cu_seqlens[mid + 1] <= t) lo = mid + 1; else hi = mid;
-  }
-  const int s = lo;
-  if (s >= a.num_seqs) return;
-  const int t_begin = a.cu_seqlens[s], t_end = a.cu_seqlens[s + 1];
-  if (t_begin < 0 || t_end > a.total_tokens || t < t_begin) return;
+  const int t_begin = a.cu_seqlens[s];
+  const int t_end = a.cu_seqlens[s + 1];
+  if (t_begin < 0 || t_end > a.total_tokens) return;
   const int n = t_end - t_begin;
   const int nrows = n * G;
-  const int i = (int)(t - t_begin);
-  const int m = i * G + h % G;
-  const int m0 = (m / kPfRows) * kPfRows;
-  const int m_last = min(m0 + kPfRows, nrows) - 1;
+  const int m0 = mt * kPfRows;
+  if (m0 >= nrows) return;
   const int L = min(a.context_lens[s], a.max_context_len);
+  const int m_last = min(m0 + kPfRows, nrows) - 1;
   const int kend = L - n + m_last / G + 1;
   const int nch = (kend + a.split_keys - 1) / a.split_keys;
   if (nch <= 1) return;  // written directly by the prefill kernel
-  const int lane = threadIdx.x;
-  const int64_t row0 = (t * a.q_heads + h) * a.max_chunks;
-  constexpr int PER = D / 64;
-  float mx = NEG_INF;
-  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.ws_lse[row0 + c]);
-  float acc[PER], den = 0.0f;
+  const int m = m0 + part * ROWS + (int)threadIdx.x / NS;
+  if (m >= nrows) return;
+  const int sl = (int)threadIdx.x % NS;
+  const int tok = t_begin + m / G;
+  const int h = g * G + m % G;
+  const int64_t row0 = ((int64_t)tok * a.q_heads + h) * a.max_chunks;
+  float mx = NEG_INF, den = 0.0f, acc[16];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  for (int c = 0; c < nch; ++c) {
-    const float lse = a.ws_lse[row0 + c];
-    if (lse == NEG_INF) continue;
-    const float w = fast_exp2(lse - mx);
-    den += w;
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  constexpr int U = 4;
+  for (int c0 = 0; c0 < nch; c0 += U) {
+    float lse[U];
+    float4 o[U][4];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, a.ws_o[(row0 + c) * D + lane + 64 * e], acc[e]);
+    for (int u = 0; u < U; ++u) {
+      const int c = min(c0 + u, nch - 1);
+      lse[u] = c0 + u < nch ? a.ws_lse[row0 + c] : NEG_INF;
+      const float4* op = reinterpret_cast<const float4*>(a.ws_o + (row0 + c) * D + sl * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[u][e] = op[e];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // a chunk with no visible key (lse = -inf) weighs nothing
+      const bool ok = lse[u] != NEG_INF;
+      const float m_new = ok ? fmaxf(mx, lse[u]) : mx;
+      const float f = ok ? fast_exp2(mx - m_new) : 1.0f;  // 0 while mx is -inf
+      const float w = ok ? fast_exp2(lse[u] - m_new) : 0.0f;
+      den = ok ? fmaf(den, f, w) : den;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[4 * e] = ok ? fmaf(acc[4 * e], f, w * o[u][e].x) : acc[4 * e];
+        acc[4 * e + 1] = ok ? fmaf(acc[4 * e + 1], f, w * o[u][e].y) : acc[4 * e + 1];
+        acc[4 * e + 2] = ok ? fmaf(acc[4 * e + 2], f, w * o[u][e].z) : acc[4 * e + 2];
+        acc[4 * e + 3] = ok ? fmaf(acc[4 * e + 3], f, w * o[u][e].w) : acc[4 * e + 3];
+      }
+      mx = m_new;
+    }
   }
-  const float inv = 1.0f / den;
-  uint16_t* op = a.out + t * a.out_st + (int64_t)h * a.out_sh;
+  const float inv = 1.0f / den;  // chunk 0 always holds key 0, so den > 0
+  uint16_t* dst = a.out + (int64_t)tok * a.out_st + (int64_t)h * a.out_sh + sl * 16;
+  uint32_t w[8];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) op[lane + 64 * e] = f32_to_bf16(acc[e] * inv);
+  for (int e = 0; e < 8; ++e)
+    w[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
+  if (a.out_aligned) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) reinterpret_cast<uint2*>(dst)[e] = make_uint2(w[2 * e], w[2 * e + 1]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dst[2 * e] = (uint16_t)w[e];
+      dst[2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
 }
 
 template <int D, int G>
@@ -451,7 +492,9 @@ static void launch_prefill_t(const pa_kv_pool_t& pool, const PrefillArgs& pa_, h
   const int64_t grid = (int64_t)a.tiles_per_seq * a.max_chunks * pool.kv_heads * pa_.num_seqs;
   prefill_kernel<D, G><<<(unsigned)grid, 256, 0, stream>>>(a);
   if (a.max_chunks > 1)
-    prefill_merge_kernel<D><<<(unsigned)(pa_.total_tokens * pa_.q_heads), 64, 0, stream>>>(a);
+    prefill_merge_kernel<D><<<(unsigned)((int64_t)(kPfRows / pf_merge_rows<D>()) *
+                                         a.tiles_per_seq * pool.kv_heads * pa_.num_seqs),
+                              256, 0, stream>>>(a);
 }
 
 template <int D>

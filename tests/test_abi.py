@@ -101,8 +101,9 @@ def test_decode_validation(lib):
     # split 16 over up to 128 tokens needs a workspace
     assert decode(lib, p, split=16, ws=0) == WORKSPACE
     need = lib.pa_decode_workspace_bytes(2, 12, 2, 128, 128, 16)
-    assert need == 2 * 12 * 8 * 129 * 4
+    assert need == 4096 + 2 * 12 * 8 * 129 * 4          # counters, then partials
     assert decode(lib, p, split=16, ws=0xC000, wsb=need - 1) == WORKSPACE
+    assert decode(lib, p, split=16, ws=0xC008, wsb=need) == WORKSPACE    # not 16-B aligned
 
 
 def test_default_split_and_workspace_bytes(lib):
@@ -116,8 +117,8 @@ def test_default_split_and_workspace_bytes(lib):
     assert ds(0, 2, 100) == 0
     wb = lib.pa_decode_workspace_bytes
     assert wb(4, 8, 2, 64, 32, 0) == 0      # one split of 32 covers every context
-    assert wb(4, 8, 2, 64, 65, 0) == 4 * 8 * 3 * 65 * 4
-    assert wb(4, 8, 2, 64, 65, 32) == 4 * 8 * 3 * 65 * 4
+    assert wb(4, 8, 2, 64, 65, 0) == 4096 + 4 * 8 * 3 * 65 * 4
+    assert wb(4, 8, 2, 64, 65, 32) == 4096 + 4 * 8 * 3 * 65 * 4
     assert wb(0, 8, 2, 64, 100, 0) == 0
     assert wb(4, 8, 2, 64, 100, -16) == 0
 
@@ -144,5 +145,6 @@ def test_prefill_validation(lib):
     need = lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 128, 64)
     assert need == 10 * 12 * 2 * 129 * 4
     assert prefill(lib, p, split=64, ws=0xE000, wsb=need - 4) == WORKSPACE
+    assert prefill(lib, p, split=64, ws=0xE004, wsb=need) == WORKSPACE  # not 16-B aligned
     assert lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 1024, 0) == 0
     assert lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 1025, 0) == 10 * 12 * 2 * 129 * 4

@@ -104,6 +104,29 @@ def test_batch_vs_single_is_bit_identical(dev):
         assert torch.equal(o1[0], out[b])
 
 
+def test_both_schedules_give_identical_bits(dev):
+    """A batch large enough for the persistent split + merge launches and each of its
+    sequences alone (single-launch schedule, cross-workgroup merge) give the same bits:
+    both merge the split partials in the same two-level order."""
+    case = W.random_case(12, B=40, Hq=16, Hkv=4, D=128, lmin=1, lmax=3000)
+    case.context_lens[:3] = [1, 100, 129]           # one split, one group, two groups
+    case.new_pos[:3] = case.context_lens[:3] - 1
+    for b in range(3):
+        p = int(case.new_pos[b])
+        case.slot_mapping[b] = int(case.block_tables[b, p // 16]) * 16 + p % 16
+    s = Setup(case, dev)
+    ws = pa.decode_workspace(40, 16, 4, 128, 3000, 16, device=dev)
+    out = pa.decode(s.q, s.pool, s.bt, s.ctx, case.scale, max_context_len=3000,
+                    split_tokens=16, workspace=ws)   # 40 x 4 x 24 groups: split + merge
+    torch.cuda.synchronize()
+    assert max_err(out, s.oracle()) <= TOL["bf16"]
+    for b in list(range(6)) + [int(np.argmax(case.context_lens))]:
+        # same workspace: the partials just written never overlap the counters
+        o1 = pa.decode(s.q[b:b + 1], s.pool, s.bt[b:b + 1], s.ctx[b:b + 1], case.scale,
+                       max_context_len=3000, split_tokens=16, workspace=ws)
+        assert torch.equal(o1[0], out[b]), b
+
+
 def test_poisoned_slots_and_tables_do_not_leak(dev):
     case = W.random_case(11, B=5, Hq=8, Hkv=2, D=128, lmin=3, lmax=500)
     clean = Setup(case, dev, poison=False)
