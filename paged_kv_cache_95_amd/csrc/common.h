@@ -69,6 +69,23 @@ __device__ __forceinline__ void e4m3x2_to_f32(uint32_t w, bool high, float& a, f
   b = r[1];
 }
 
+// Two e4m3fn codes (bytes 0,1 or 2,3 of w) -> their bf16 pair (exact: every e4m3fn
+// value, subnormals included, is a bf16 value; the unit scale leaves them unchanged).
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool high) {
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  const bf2_t r = high ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two fp32 values rounded to nearest even into a bf16 pair (lo, hi).
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf2 bf16x2_rne(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  const f2_t x = {lo, hi};
+  return __builtin_convertvector(x, bf2);
+}
+
 // Pack the bf16 images of two fp32 values that are exactly representable in bf16
 // (low half = lo, high half = hi).
 __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {

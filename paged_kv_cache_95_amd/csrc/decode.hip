@@ -79,11 +79,11 @@ struct BlockBuf {
   int nvalid;
 };
 
-// Blocks kept in flight per wave: three where the registers allow it without losing a
-// wave per SIMD, else two.
+// Blocks kept in flight per wave: as many as the registers allow without losing a
+// wave per SIMD (an FP8 block buffer is half the size of a bf16 one).
 template <int KVT, int G>
 struct RingDepth {
-  static constexpr int value = G <= 4 ? 3 : 2;
+  static constexpr int value = KVT == kFP8 ? (G <= 4 ? 4 : (G <= 6 ? 3 : 2)) : (G <= 4 ? 3 : 2);
 };
 
 template <int KVT, int D, int G>
@@ -119,10 +119,8 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
     } else if constexpr (KVT == kFP8) {
 #pragma unroll
       for (int w = 0; w < Gm::KC * 4; ++w) {
-        float x0, x1, x2, x3;
-        e4m3x2_to_f32(b.k[k][w], false, x0, x1);
-        e4m3x2_to_f32(b.k[k][w], true, x2, x3);
-        const uint32_t p0 = pack_bf16_exact(x0, x1), p1 = pack_bf16_exact(x2, x3);
+        const uint32_t p0 = e4m3x2_to_bf16x2(b.k[k][w], false);
+        const uint32_t p1 = e4m3x2_to_bf16x2(b.k[k][w], true);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           s[k][h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][2 * w]),
@@ -191,6 +189,38 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
       }
   }
   // ---- V: the row's four tokens (own set 0, other set 0, own set 1, other set 1)
+  if constexpr (KVT == kFP8) {
+    // Token pairs (own, other) of each set: per head dim, the two tokens' values form
+    // one bf16 pair (FP8 codes are exact in bf16), the two probabilities another
+    // (rounded once to bf16), and one dot2 does both multiply-adds in fp32.
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float va[Gm::EV], vb[Gm::EV];
+      const bool ok_a = !MASKED || tok_v[2 * k] < b.nvalid;
+      const bool ok_b = !MASKED || tok_v[2 * k + 1] < b.nvalid;
+#pragma unroll
+      for (int w = 0; w < Gm::VW; ++w) {
+        const uint32_t ya = ok_a ? b.v[2 * k][w] : 0u;  // invalid tokens: exact zeros
+        const uint32_t yb = ok_b ? b.v[2 * k + 1][w] : 0u;
+        e4m3x2_to_f32(ya, false, va[4 * w], va[4 * w + 1]);
+        e4m3x2_to_f32(ya, true, va[4 * w + 2], va[4 * w + 3]);
+        e4m3x2_to_f32(yb, false, vb[4 * w], vb[4 * w + 1]);
+        e4m3x2_to_f32(yb, true, vb[4 * w + 2], vb[4 * w + 3]);
+      }
+      uint32_t vp[Gm::EV];
+#pragma unroll
+      for (int e = 0; e < Gm::EV; ++e) vp[e] = pack_bf16_exact(va[e], vb[e]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const bf2 pp = bf16x2_rne(p_own[k][h], p_oth[k][h]);
+#pragma unroll
+        for (int e = 0; e < Gm::EV; ++e)
+          st.acc[h][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf2, vp[e]),
+                                                         st.acc[h][e], false);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     const bool valid_v = !MASKED || tok_v[x] < b.nvalid;
@@ -201,13 +231,6 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
         const uint32_t y = valid_v ? b.v[x][w] : 0u;
         vf[2 * w] = bf16_lo(y);
         vf[2 * w + 1] = bf16_hi(y);
-      }
-    } else if constexpr (KVT == kFP8) {
-#pragma unroll
-      for (int w = 0; w < Gm::VW; ++w) {
-        const uint32_t y = valid_v ? b.v[x][w] : 0u;
-        e4m3x2_to_f32(y, false, vf[4 * w], vf[4 * w + 1]);
-        e4m3x2_to_f32(y, true, vf[4 * w + 2], vf[4 * w + 3]);
       }
     } else {
 #pragma unroll
@@ -525,6 +548,19 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(SplitArgs a) 
 // padding the grid to max_context_len would launch mostly empty workgroups.
 constexpr int kMaxCompactSeqs = 4096;
 
+// Partials are merged in groups of this many consecutive splits (see the merge below).
+constexpr int kGroupSplits = 8;
+// Calls with at most this many (sequence, group, KV head) workgroups take the single-
+// launch schedule; larger ones the persistent split kernel plus a merge launch.
+constexpr int64_t kFusedMaxWorkgroups = 1024;
+// Words of the workspace's counter block: the single-launch schedule uses one per
+// (sequence, KV head) and only when a sequence has two or more groups, so at most
+// kFusedMaxWorkgroups / 2 of them; the persistent schedule's work counter and
+// leaver count use the last two.
+constexpr int kCompactQueueWord = kDecodeCounters - 2;
+constexpr int kCompactDoneWord = kDecodeCounters - 1;
+static_assert(kFusedMaxWorkgroups / 2 <= kCompactQueueWord, "counter words overlap");
+
 __device__ __forceinline__ int block_exclusive_scan(int x, int* wave_sums, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = x;
@@ -565,25 +601,57 @@ __global__ void __launch_bounds__(64 * kWaves) decode_compact_kernel(SplitArgs a
   __syncthreads();
   const int64_t entries = (int64_t)carry * a.hkv;
   const int64_t steps = (entries + kWaves - 1) / kWaves;
-  const int64_t first = (int64_t)blockIdx.x * steps / gridDim.x;
-  const int64_t last = ((int64_t)blockIdx.x + 1) * steps / gridDim.x;
-  int s = 0;
-  for (int64_t st = first; st < last; ++st) {
+  // the four items of workgroup step st (one per wave)
+  auto run_step = [&](int64_t st) {
     const int64_t e = st * kWaves + wave;
-    if (e >= entries) break;
+    if (e >= entries) return;
     const int g = (int)(e % a.hkv);
     const int pair = (int)(e / a.hkv);
-    if (st == first) {
-      // largest s with cum[s] <= pair (sequences without splits have cum[s] == cum[s+1])
-      int lo = 0, hi = a.num_seqs - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cum[mid] <= pair) lo = mid; else hi = mid - 1;
-      }
-      s = lo;
+    // largest s with cum[s] <= pair (sequences without splits have cum[s] == cum[s+1])
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cum[mid] <= pair) lo = mid; else hi = mid - 1;
     }
-    while (cum[s + 1] <= pair) ++s;
-    decode_item<KVT, D, G, QT>(a, s, pair - cum[s], g, lane);
+    decode_item<KVT, D, G, QT>(a, lo, pair - cum[lo], g, lane);
+  };
+  if (a.counters == nullptr) {
+    // no workspace (every context fits one split): the b-th contiguous share of steps
+    const int64_t first = (int64_t)blockIdx.x * steps / gridDim.x;
+    const int64_t last = ((int64_t)blockIdx.x + 1) * steps / gridDim.x;
+    for (int64_t st = first; st < last; ++st) run_step(st);
+    return;
+  }
+  // Steps are handed out by a device-wide counter, so workgroups that drew short items
+  // take more of them and the call ends with at most one step of imbalance. The next
+  // step is drawn while the current one runs. The last workgroup to leave returns the
+  // counters to zero for the next call.
+  unsigned* queue = a.counters + kCompactQueueWord;
+  unsigned* done = a.counters + kCompactDoneWord;
+  __shared__ unsigned next_step;
+  unsigned nxt = 0;
+  if (threadIdx.x == 0) {
+    nxt = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    next_step = nxt;
+  }
+  __syncthreads();
+  int64_t st = next_step;
+  while (st < steps) {
+    if (threadIdx.x == 0)
+      nxt = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    run_step(st);
+    __syncthreads();  // every wave has read next_step for this round
+    if (threadIdx.x == 0) next_step = nxt;
+    __syncthreads();
+    st = next_step;
+  }
+  if (threadIdx.x == 0) {
+    const unsigned d = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == gridDim.x - 1) {
+      // every workgroup has drawn its last (out of range) step: reset for the next call
+      __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -597,10 +665,6 @@ __global__ void __launch_bounds__(64 * kWaves) decode_compact_kernel(SplitArgs a
 //                       group partial o_c = acc * (1/den), lse_c = M + log2(den)
 //   level 2:            the same online merge over the groups, out = acc * (1/den).
 // A sequence with a single group writes level 1's acc * (1/den) directly.
-constexpr int kGroupSplits = 8;
-// Calls with at most this many (sequence, group, KV head) workgroups take the single-
-// launch schedule; larger ones the persistent split kernel plus a merge launch.
-constexpr int64_t kFusedMaxWorkgroups = 1024;
 
 struct Merge4 {
   float m, den, acc[4];

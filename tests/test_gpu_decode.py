@@ -278,18 +278,21 @@ def test_workspace_reuse_across_calls(dev):
         assert max_err(out, s.oracle()) <= TOL["bf16"]
 
 
-def test_graph_replay_matches_eager(dev):
+@pytest.mark.parametrize("B,Hkv,split", [(6, 2, 64), (40, 4, 16)])
+def test_graph_replay_matches_eager(dev, B, Hkv, split):
     """Store + decode captured in a HIP graph: every replay, with eager work and
-    synchronisations in between, reproduces the eager result bit for bit."""
-    case = W.random_case(56, B=6, Hq=12, Hkv=2, D=128, lmin=100, lmax=2500)
+    synchronisations in between, reproduces the eager result bit for bit. The small
+    batch runs the single-launch schedule (its arrival counters must return to zero),
+    the large one the persistent schedule (its work counter must too)."""
+    case = W.random_case(56, B=B, Hq=3 * Hkv * 2, Hkv=Hkv, D=128, lmin=100, lmax=2500)
     s = Setup(case, dev)
-    ws = pa.decode_workspace(6, 12, 2, 128, 2500, 64, device=dev)
+    ws = pa.decode_workspace(B, 6 * Hkv, Hkv, 128, 2500, split, device=dev)
     out = torch.empty_like(s.q)
 
     def step():
         pa.store_kv(s.pool, s.k_new, s.v_new, s.slots)
-        pa.decode(s.q, s.pool, s.bt, s.ctx, case.scale, max_context_len=2500, split_tokens=64,
-                  out=out, workspace=ws)
+        pa.decode(s.q, s.pool, s.bt, s.ctx, case.scale, max_context_len=2500,
+                  split_tokens=split, out=out, workspace=ws)
 
     step()
     torch.cuda.synchronize()
