@@ -31,6 +31,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV GB/s (% of HBM peak) + decode seqs/sec per step"
+# HBM bytes per launch of the headline decode kernel, read with rocprofv3 FETCH_SIZE /
+# WRITE_SIZE (calibrated against a copy) and recorded in this profile summary together
+# with a hash of the decode sources they were taken with.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_qwen_28layer.md")
+DECODE_SOURCES = ["paged_kv_cache_95_amd/csrc/decode.hip", "paged_kv_cache_95_amd/csrc/common.h",
+                  "paged_kv_cache_95_amd/csrc/internal.h"]
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 LAYERS = 28
@@ -61,6 +67,29 @@ def prefill_flops(n, P, hq, d):
     """Causal pairs only: row i of a chunk on prefix P sees P + i + 1 keys; 2 matmuls."""
     pairs = sum(int(ni) * int(pi) + int(ni) * (int(ni) + 1) // 2 for ni, pi in zip(n, P))
     return 4 * d * hq * pairs
+
+
+def decode_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Counter-measured HBM bytes per launch of the headline decode kernel, or None when
+    the profile is missing or was taken with other decode sources."""
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch=(\d+) decode_sources_sha256=([0-9a-f]{64})", text)
+    if not m or m.group(2) != decode_sources_sha256():
+        return None
+    return int(m.group(1))
 
 
 # ----------------------------------------------------------------------------- timing
@@ -347,13 +376,17 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "per_layer": {"decode_ms": round(dec_ms, 5), "store_ms": round(sto_ms, 5),
                       "decode_bytes": dby, "store_bytes": sby},
-        "roofline": {"kernel": "decode_split_kernel<bf16, D128, G6>", "bound": "hbm",
+        "roofline": {"kernel": "decode_fused_kernel<bf16, D128, G6> (single-launch decode)",
+                     "bound": "hbm",
                      "achieved": round(dby / dec_ms / 1e6, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dby / dec_ms / 1e6 / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "per_launch_bytes": dby,
+                     "traffic": recorded_traffic(),
+                     "per_launch_bytes": dby, "per_launch_us": round(dec_ms * 1e3, 2),
                      "note": "achieved = algorithmic bytes of one decode launch / its average "
-                             "duration (graph of 28 decode launches, HIP events)"},
+                             "duration (HIP events around a graph of the 28 layers' decode "
+                             "launches alone); traffic = HBM bytes per launch from rocprofv3 "
+                             "FETCH_SIZE x2 + WRITE_SIZE (copy-calibrated), null if the decode "
+                             "sources changed since"},
     }
     if not args.no_extra:
         log("extra: large decode")
