@@ -203,6 +203,36 @@ int pa_decode(void *out, int64_t out_stride_tok, int64_t out_stride_head, const 
               void *stream);
 
 /*
+ * pa_decode_step - one decode step of a layer: store each sequence's new K/V row, then
+ * attend, with the same result as pa_store_kv followed by pa_decode.
+ *
+ * Defined by [P4] "KV Cache management" / "CUDA Graph" (a decode step writes the new
+ * token's K/V to its slot through slot_mapping, then the paged decode kernel attends
+ * the context including it; "errors, type 1": the context counts the new token).
+ * Arguments are those of pa_decode plus the new rows of pa_store_kv with num_tokens =
+ * num_seqs: row s of k_new / v_new ([num_seqs, kv_heads, head_dim] of src_dtype,
+ * element strides, innermost stride 1) is sequence s's new token and slot_mapping[s]
+ * (int64) its slot, or < 0 for a sequence without a new token this step.
+ * Contract: a slot >= 0 must be the slot of position context_lens[s] - 1 (the new token
+ * is the last token of the context). Otherwise the bytes written are still exactly
+ * those of pa_store_kv, but that sequence's output is unspecified.
+ * For small batches with bf16/fp32 pools and rows starting on 16 bytes, the store is
+ * folded into the single decode launch (the new token is read from k_new / v_new while
+ * its slot is written); otherwise a store launch runs first. Either way the output and
+ * the pool bytes are identical to the two calls. Workspace as for pa_decode.
+ */
+int pa_decode_step(void *out, int64_t out_stride_tok, int64_t out_stride_head, const void *q,
+                   int64_t q_stride_tok, int64_t q_stride_head, int32_t q_dtype,
+                   int32_t num_seqs, int32_t q_heads, const pa_kv_pool_t *pool,
+                   const void *k_new, const void *v_new, int32_t src_dtype,
+                   int64_t k_stride_tok, int64_t k_stride_head, int64_t v_stride_tok,
+                   int64_t v_stride_head, const int64_t *slot_mapping,
+                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                   const int32_t *context_lens, int32_t max_context_len, float scale,
+                   int32_t split_tokens, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/*
  * pa_varlen_prefill - causal attention for a flat batch of query chunks.
  *
  * Defined by [P5] "varlen batch" / "cu_seqlens is only needed in attention" (tokens of

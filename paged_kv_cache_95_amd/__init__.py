@@ -55,6 +55,9 @@ SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32,
                                  ctypes.POINTER(_Pool), _P, _I32, _P, _I32, _F, _I32, _P, _SZ,
                                  _P]),
+    "pa_decode_step": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32,
+                                      ctypes.POINTER(_Pool), _P, _P, _I32, _I64, _I64, _I64,
+                                      _I64, _P, _P, _I32, _P, _I32, _F, _I32, _P, _SZ, _P]),
     "pa_varlen_prefill_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
     "pa_varlen_prefill": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _P, _I32, _I64,
                                          _I32, _I32, ctypes.POINTER(_Pool), _P, _I32, _P, _I32,
@@ -210,6 +213,40 @@ def decode(q, pool, block_tables, context_lens, scale, max_context_len=None, spl
                            _ptr(context_lens), int(max_context_len), float(scale),
                            int(split_tokens), _ptr(workspace), wbytes, _stream()),
            "pa_decode")
+    return out
+
+
+def decode_step(q, pool, k_new, v_new, slot_mapping, block_tables, context_lens, scale,
+                max_context_len=None, split_tokens=0, out=None, workspace=None):
+    """One decode step: store row s of k_new / v_new [B, kv_heads, head_dim] at
+    slot_mapping[s] (int64; negative = no new token), then attend as decode(); the same
+    result as store_kv() followed by decode(), in one launch for small batches."""
+    _meta(block_tables, context_lens)
+    B, Hq, D = q.shape
+    ks, vs = _rows3(k_new, "k_new"), _rows3(v_new, "v_new")
+    _need(k_new.shape == v_new.shape and k_new.shape == (B, pool.kv_heads, pool.head_dim),
+          "k_new/v_new shape [B, kv_heads, head_dim]")
+    _need(k_new.dtype == v_new.dtype, "k_new/v_new dtype")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1
+          and slot_mapping.shape[0] == B and slot_mapping.is_contiguous(),
+          "slot_mapping must be contiguous int64 [B]")
+    if max_context_len is None:
+        max_context_len = block_tables.shape[1] * pool.block_size
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    qs, os_ = _rows3(q, "q"), _rows3(out, "out")
+    need = decode_workspace_bytes(B, Hq, pool.kv_heads, D, max_context_len, split_tokens)
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_decode_step(_ptr(out), os_[0], os_[1], _ptr(q), qs[0], qs[1],
+                                _DTYPE_CODE[q.dtype], B, Hq, pool.struct, _ptr(k_new),
+                                _ptr(v_new), _DTYPE_CODE[k_new.dtype], ks[0], ks[1], vs[0],
+                                vs[1], _ptr(slot_mapping), _ptr(block_tables),
+                                block_tables.shape[1], _ptr(context_lens), int(max_context_len),
+                                float(scale), int(split_tokens), _ptr(workspace), wbytes,
+                                _stream()),
+           "pa_decode_step")
     return out
 
 

@@ -46,6 +46,18 @@ int effective_split(int split_tokens, int64_t num_seqs, int kv_heads, int max_co
   return split;
 }
 
+// Source rows of pa_store_kv / pa_decode_step: dtype pairing and strides.
+int check_store_rows(const pa_kv_pool_t* pool, int32_t src_dtype, int64_t k_stride_tok,
+                     int64_t k_stride_head, int64_t v_stride_tok, int64_t v_stride_head) {
+  const bool src_ok = pool->dtype == PA_FP8_E4M3
+                          ? (src_dtype == PA_BF16 || src_dtype == PA_F32)
+                          : src_dtype == pool->dtype;
+  if (!src_ok) return PA_ERR_INVALID_ARG;
+  if (k_stride_tok < 0 || k_stride_head < 0 || v_stride_tok < 0 || v_stride_head < 0)
+    return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
 int launched(int status) {
   if (status != PA_OK) return status;
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -93,25 +105,29 @@ int pa_store_kv(const pa_kv_pool_t* pool, const void* k, const void* v, int32_t 
   int status = PA_OK;
   if (!pool_shape_ok(pool, &status)) return status;
   if (num_tokens < 0) return PA_ERR_INVALID_ARG;
-  const bool src_ok = pool->dtype == PA_FP8_E4M3
-                          ? (src_dtype == PA_BF16 || src_dtype == PA_F32)
-                          : src_dtype == pool->dtype;
-  if (!src_ok) return PA_ERR_INVALID_ARG;
-  if (k_stride_tok < 0 || k_stride_head < 0 || v_stride_tok < 0 || v_stride_head < 0)
-    return PA_ERR_INVALID_ARG;
-  if (num_tokens == 0) return PA_OK;
+  status = check_store_rows(pool, src_dtype, k_stride_tok, k_stride_head, v_stride_tok,
+                            v_stride_head);
+  if (status != PA_OK || num_tokens == 0) return status;
   if (!k || !v || !slot_mapping) return PA_ERR_INVALID_ARG;
   return launched(pa::launch_store(*pool, k, v, src_dtype, num_tokens, k_stride_tok,
                                    k_stride_head, v_stride_tok, v_stride_head, slot_mapping,
                                    (hipStream_t)stream));
 }
 
-int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const void* q,
-              int64_t q_stride_tok, int64_t q_stride_head, int32_t q_dtype, int32_t num_seqs,
-              int32_t q_heads, const pa_kv_pool_t* pool, const int32_t* block_tables,
-              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
-              float scale, int32_t split_tokens, void* workspace, size_t workspace_bytes,
-              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and argument block shared by pa_decode and pa_decode_step. Returns PA_OK
+// with *nothing = true when there is no sequence to decode.
+int prepare_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const void* q,
+                   int64_t q_stride_tok, int64_t q_stride_head, int32_t q_dtype,
+                   int32_t num_seqs, int32_t q_heads, const pa_kv_pool_t* pool,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, int32_t max_context_len, float scale,
+                   int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                   pa::DecodeArgs* a, bool* nothing) {
+  *nothing = false;
   int status = PA_OK;
   if (!pool_shape_ok(pool, &status)) return status;
   if (num_seqs < 0 || q_heads <= 0 || q_heads % pool->kv_heads != 0) return PA_ERR_INVALID_ARG;
@@ -122,7 +138,7 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
   if (split_tokens < 0 || split_tokens % kBlockSize != 0 || split_tokens > kMaxSplitTokens)
     return PA_ERR_INVALID_ARG;
   if (!(scale > 0.0f) || scale > 3.0e38f) return PA_ERR_INVALID_ARG;  // finite, positive
-  if (num_seqs == 0) return PA_OK;
+  if (num_seqs == 0) return *nothing = true, PA_OK;
   if (!out || !q || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
   if (max_blocks_per_seq <= 0 || max_context_len <= 0 ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlockSize)
@@ -137,28 +153,80 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
   if (grid >= (int64_t)1 << 31 || (int64_t)num_seqs * q_heads >= (int64_t)1 << 31)
     return PA_ERR_UNSUPPORTED;
 
-  pa::DecodeArgs a;
-  a.out = out;
-  a.out_st = out_stride_tok;
-  a.out_sh = out_stride_head;
-  a.q = q;
-  a.q_st = q_stride_tok;
-  a.q_sh = q_stride_head;
-  a.num_seqs = num_seqs;
-  a.q_heads = q_heads;
-  a.block_tables = block_tables;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.context_lens = context_lens;
-  a.max_context_len = max_context_len;
-  a.scale = scale;
-  a.split_tokens = split;
-  a.max_splits = max_splits;
+  a->out = out;
+  a->out_st = out_stride_tok;
+  a->out_sh = out_stride_head;
+  a->q = q;
+  a->q_st = q_stride_tok;
+  a->q_sh = q_stride_head;
+  a->num_seqs = num_seqs;
+  a->q_heads = q_heads;
+  a->block_tables = block_tables;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->context_lens = context_lens;
+  a->max_context_len = max_context_len;
+  a->scale = scale;
+  a->split_tokens = split;
+  a->max_splits = max_splits;
   // workspace: [arrival counters, fixed 4 KiB][o: num_seqs, q_heads, max_splits, D][lse]
-  a.counters = need > 0 ? (unsigned*)workspace : nullptr;
-  a.ws_o = need > 0 ? (float*)((char*)workspace + pa::kDecodeCounterBytes) : nullptr;
-  a.ws_lse = need > 0 ? a.ws_o + (size_t)num_seqs * q_heads * max_splits * pool->head_dim
-                      : nullptr;
+  a->counters = need > 0 ? (unsigned*)workspace : nullptr;
+  a->ws_o = need > 0 ? (float*)((char*)workspace + pa::kDecodeCounterBytes) : nullptr;
+  a->ws_lse = need > 0 ? a->ws_o + (size_t)num_seqs * q_heads * max_splits * pool->head_dim
+                       : nullptr;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const void* q,
+              int64_t q_stride_tok, int64_t q_stride_head, int32_t q_dtype, int32_t num_seqs,
+              int32_t q_heads, const pa_kv_pool_t* pool, const int32_t* block_tables,
+              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+              float scale, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  pa::DecodeArgs a;
+  bool nothing = false;
+  const int st = prepare_decode(out, out_stride_tok, out_stride_head, q, q_stride_tok,
+                                q_stride_head, q_dtype, num_seqs, q_heads, pool, block_tables,
+                                max_blocks_per_seq, context_lens, max_context_len, scale,
+                                split_tokens, workspace, workspace_bytes, &a, &nothing);
+  if (st != PA_OK || nothing) return st;
   return launched(pa::launch_decode(*pool, a, (hipStream_t)stream));
+}
+
+int pa_decode_step(void* out, int64_t out_stride_tok, int64_t out_stride_head, const void* q,
+                   int64_t q_stride_tok, int64_t q_stride_head, int32_t q_dtype,
+                   int32_t num_seqs, int32_t q_heads, const pa_kv_pool_t* pool,
+                   const void* k_new, const void* v_new, int32_t src_dtype,
+                   int64_t k_stride_tok, int64_t k_stride_head, int64_t v_stride_tok,
+                   int64_t v_stride_head, const int64_t* slot_mapping,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, int32_t max_context_len, float scale,
+                   int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  pa::DecodeArgs a;
+  bool nothing = false;
+  int st = prepare_decode(out, out_stride_tok, out_stride_head, q, q_stride_tok, q_stride_head,
+                          q_dtype, num_seqs, q_heads, pool, block_tables, max_blocks_per_seq,
+                          context_lens, max_context_len, scale, split_tokens, workspace,
+                          workspace_bytes, &a, &nothing);
+  if (st != PA_OK) return st;
+  st = check_store_rows(pool, src_dtype, k_stride_tok, k_stride_head, v_stride_tok,
+                        v_stride_head);
+  if (st != PA_OK || nothing) return st;
+  if (!k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  pa::StepRows rows;
+  rows.k = k_new;
+  rows.v = v_new;
+  rows.src_dtype = src_dtype;
+  rows.k_st = k_stride_tok;
+  rows.k_sh = k_stride_head;
+  rows.v_st = v_stride_tok;
+  rows.v_sh = v_stride_head;
+  rows.slots = slot_mapping;
+  return launched(pa::launch_decode_step(*pool, a, rows, (hipStream_t)stream));
 }
 
 size_t pa_varlen_prefill_workspace_bytes(int64_t total_tokens, int32_t q_heads,

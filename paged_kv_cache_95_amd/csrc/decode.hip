@@ -268,6 +268,13 @@ struct SplitArgs {
   float* ws_lse;     // [num_seqs, q_heads, max_splits]
   int max_chunks;    // ceil(max_splits / kGroupSplits): groups per sequence, at most
   unsigned* counters;  // [num_seqs, kv_heads] arrival counters, zero between calls
+  // Decode step with the store folded in (single-launch schedule only; knew == nullptr
+  // otherwise): row s of knew / vnew ([num_seqs, kv_heads, D] of the pool dtype, element
+  // strides, 16-byte aligned rows) is sequence s's newest token, stored to slots[s].
+  const char* knew;
+  const char* vnew;
+  int64_t knew_st, knew_sh, vnew_st, vnew_sh;
+  const int64_t* slots;
   bool q_aligned;    // q rows start on 16-byte boundaries (base and strides)
   bool out_aligned;  // same for out
 };
@@ -348,10 +355,14 @@ __device__ __forceinline__ void load_item_inputs(const SplitArgs& a, int s, int 
 // attention for the G heads of group g, normalised (o = sum p v / sum p) with its
 // log2-sum-exp, in lanes 0..15 (lane c holds head dims [c*D/16, (c+1)*D/16)). A split
 // past the context (possible in the fused schedule) yields lse2 = -inf.
+// krow_new / vrow_new (may be null): the K / V row of the context's last token taken
+// from the step's input instead of the pool, where a concurrent store is writing it.
 template <int KVT, int D, int G>
 __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KVT, D, G>& in,
                                              int split, int g, int L, int lane,
-                                             float (&o)[G][Geom<KVT, D>::EV], float (&lse2)[G]) {
+                                             float (&o)[G][Geom<KVT, D>::EV], float (&lse2)[G],
+                                             const char* krow_new = nullptr,
+                                             const char* vrow_new = nullptr) {
   using Gm = Geom<KVT, D>;
   constexpr float NEG_INF = -__builtin_huge_valf();
   const int t0 = split * a.split_tokens;
@@ -391,19 +402,25 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
     const int64_t bid = ok ? bid_raw : 0;
     const int first = (jb0 + j) * kBlockSize;
     b.nvalid = ok ? min(kBlockSize, L - first) : 0;
+    // position of the step's new token in this block (only the context's last block
+    // has one in [0, 16)); lanes holding it read the input row instead of the pool
+    const int pnew = krow_new != nullptr ? L - 1 - first : -1;
     const char* kb = a.kpool + bid * blk_bytes;
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 2; ++k) {
+      const char* kp = tok_k[k] == pnew ? krow_new + t8 * 16 : kb + kofs[k];
 #pragma unroll
       for (int c = 0; c < Gm::KC; ++c) {
         uint4 x = make_uint4(0, 0, 0, 0);
-        if (k_lane) x = ld_stream16(kb + kofs[k] + c * 128);
+        if (k_lane) x = ld_stream16(kp + c * 128);
         b.k[k][4 * c] = x.x; b.k[k][4 * c + 1] = x.y; b.k[k][4 * c + 2] = x.z;
         b.k[k][4 * c + 3] = x.w;
       }
+    }
     const char* vb = a.vpool + bid * blk_bytes;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) load_dwords<Gm::VW>(vb + vofs[x], b.v[x]);
+    for (int x = 0; x < 4; ++x)
+      load_dwords<Gm::VW>(tok_v[x] == pnew ? vrow_new + cv * Gm::VB : vb + vofs[x], b.v[x]);
     if constexpr (KVT == kFP8) {
       const int64_t sb = bid * kBlockSize * a.hkv;
 #pragma unroll
@@ -835,12 +852,30 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   const int split = c * NW + wave;
   ItemIn<KVT, D, G> in;
   load_item_inputs<KVT, D, G, QT>(a, s, split, g, lane, in);
+  const char* krow_new = nullptr;
+  const char* vrow_new = nullptr;
+  if (a.knew != nullptr) {
+    // decode step: group 0 of (s, g) stores the new K/V row (waves 0 and 1, 16 bytes
+    // per lane); every wave reads that row from the input, not from the pool
+    const int64_t slot = a.slots[s];
+    if (slot >= 0) {
+      krow_new = a.knew + ((int64_t)s * a.knew_st + (int64_t)g * a.knew_sh) * Gm::E;
+      vrow_new = a.vnew + ((int64_t)s * a.vnew_st + (int64_t)g * a.vnew_sh) * Gm::E;
+      if (c == 0 && wave < 2 && lane < Gm::NCH && slot < a.num_blocks * kBlockSize) {
+        const int64_t off = (slot / kBlockSize) * kBlockSize * a.hkv * Gm::ROW +
+                            ((slot % kBlockSize) * a.hkv + g) * Gm::ROW + lane * 16;
+        const char* src = (wave == 0 ? krow_new : vrow_new) + lane * 16;
+        char* dst = const_cast<char*>(wave == 0 ? a.kpool : a.vpool) + off;
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      }
+    }
+  }
   const int L = clamped_len(a, s);
   const int nsplit = num_splits(L, a.split_tokens);
   const int ngroups = (nsplit + NW - 1) / NW;
   if (c >= ngroups) return;  // uniform over the workgroup, before any barrier
   float o[G][Gm::EV], lse2[G];
-  item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2);
+  item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2, krow_new, vrow_new);
   if (lane < 16) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -911,8 +946,12 @@ static int64_t resident_workgroups(K kernel) {
   return (int64_t)cus * per_cu;
 }
 
+// step != nullptr: a decode step whose new rows are stored first (folded into the
+// single-launch kernel when that schedule runs and the rows allow it, else a store
+// launch ahead of the decode).
 template <int KVT, int D, int G, int QT>
-static void launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream) {
+static int launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, const StepRows* step,
+                           hipStream_t stream) {
   SplitArgs sa;
   sa.kpool = (const char*)pool.k;
   sa.vpool = (const char*)pool.v;
@@ -944,11 +983,27 @@ static void launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, hipSt
   sa.out_aligned = al(a.out, a.out_st, a.out_sh, qe);
   sa.max_chunks = (a.max_splits + kGroupSplits - 1) / kGroupSplits;
   sa.counters = a.counters;
+  sa.knew = sa.vnew = nullptr;
+  sa.knew_st = sa.knew_sh = sa.vnew_st = sa.vnew_sh = 0;
+  sa.slots = nullptr;
   const int64_t fused_groups = (int64_t)a.num_seqs * pool.kv_heads * sa.max_chunks;
+  if (step != nullptr && fused_groups <= kFusedMaxWorkgroups) {
+    sa.knew = (const char*)step->k;
+    sa.vnew = (const char*)step->v;
+    sa.knew_st = step->k_st;
+    sa.knew_sh = step->k_sh;
+    sa.vnew_st = step->v_st;
+    sa.vnew_sh = step->v_sh;
+    sa.slots = step->slots;
+  } else if (step != nullptr) {
+    const int st = launch_store(pool, step->k, step->v, step->src_dtype, a.num_seqs, step->k_st,
+                                step->k_sh, step->v_st, step->v_sh, step->slots, stream);
+    if (st != PA_OK) return st;
+  }
   static_assert(kFusedMaxWorkgroups <= kDecodeCounters, "one counter per (sequence, KV head)");
   if (fused_groups <= kFusedMaxWorkgroups) {
     decode_fused_kernel<KVT, D, G, QT><<<(unsigned)fused_groups, 64 * kGroupSplits, 0, stream>>>(sa);
-    return;
+    return PA_OK;
   }
   const int64_t items = (int64_t)a.num_seqs * a.max_splits * pool.kv_heads;
   const int64_t steps = (items + kWaves - 1) / kWaves;  // upper bound of workgroup steps
@@ -962,38 +1017,64 @@ static void launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, hipSt
   if (a.max_splits > 1)
     decode_merge_kernel<D, G, QT><<<(unsigned)((int64_t)a.num_seqs * pool.kv_heads),
                                     kMergeThreads, 0, stream>>>(sa);
+  return PA_OK;
 }
 
 template <int KVT, int D, int QT>
-static int dispatch_g(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream) {
+static int dispatch_g(const pa_kv_pool_t& pool, const DecodeArgs& a, const StepRows* step,
+                      hipStream_t stream) {
   switch (a.q_heads / pool.kv_heads) {
-    case 1: launch_decode_t<KVT, D, 1, QT>(pool, a, stream); return PA_OK;
-    case 2: launch_decode_t<KVT, D, 2, QT>(pool, a, stream); return PA_OK;
-    case 3: launch_decode_t<KVT, D, 3, QT>(pool, a, stream); return PA_OK;
-    case 4: launch_decode_t<KVT, D, 4, QT>(pool, a, stream); return PA_OK;
-    case 5: launch_decode_t<KVT, D, 5, QT>(pool, a, stream); return PA_OK;
-    case 6: launch_decode_t<KVT, D, 6, QT>(pool, a, stream); return PA_OK;
-    case 7: launch_decode_t<KVT, D, 7, QT>(pool, a, stream); return PA_OK;
-    case 8: launch_decode_t<KVT, D, 8, QT>(pool, a, stream); return PA_OK;
+    case 1: return launch_decode_t<KVT, D, 1, QT>(pool, a, step, stream);
+    case 2: return launch_decode_t<KVT, D, 2, QT>(pool, a, step, stream);
+    case 3: return launch_decode_t<KVT, D, 3, QT>(pool, a, step, stream);
+    case 4: return launch_decode_t<KVT, D, 4, QT>(pool, a, step, stream);
+    case 5: return launch_decode_t<KVT, D, 5, QT>(pool, a, step, stream);
+    case 6: return launch_decode_t<KVT, D, 6, QT>(pool, a, step, stream);
+    case 7: return launch_decode_t<KVT, D, 7, QT>(pool, a, step, stream);
+    case 8: return launch_decode_t<KVT, D, 8, QT>(pool, a, step, stream);
     default: return PA_ERR_UNSUPPORTED;
   }
 }
 
-int launch_decode(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream) {
+static int dispatch(const pa_kv_pool_t& pool, const DecodeArgs& a, const StepRows* step,
+                    hipStream_t stream) {
   const int D = pool.head_dim;
   switch (pool.dtype) {
     case PA_F32:
-      return D == 64 ? dispatch_g<kF32, 64, kF32>(pool, a, stream)
-                     : dispatch_g<kF32, 128, kF32>(pool, a, stream);
+      return D == 64 ? dispatch_g<kF32, 64, kF32>(pool, a, step, stream)
+                     : dispatch_g<kF32, 128, kF32>(pool, a, step, stream);
     case PA_BF16:
-      return D == 64 ? dispatch_g<kBF16, 64, kBF16>(pool, a, stream)
-                     : dispatch_g<kBF16, 128, kBF16>(pool, a, stream);
+      return D == 64 ? dispatch_g<kBF16, 64, kBF16>(pool, a, step, stream)
+                     : dispatch_g<kBF16, 128, kBF16>(pool, a, step, stream);
     case PA_FP8_E4M3:
-      return D == 64 ? dispatch_g<kFP8, 64, kBF16>(pool, a, stream)
-                     : dispatch_g<kFP8, 128, kBF16>(pool, a, stream);
+      return D == 64 ? dispatch_g<kFP8, 64, kBF16>(pool, a, step, stream)
+                     : dispatch_g<kFP8, 128, kBF16>(pool, a, step, stream);
     default:
       return PA_ERR_UNSUPPORTED;
   }
+}
+
+int launch_decode(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream) {
+  return dispatch(pool, a, nullptr, stream);
+}
+
+int launch_decode_step(const pa_kv_pool_t& pool, const DecodeArgs& a, const StepRows& rows,
+                       hipStream_t stream) {
+  // the store folds into the single-launch kernel for same-dtype rows that start on 16
+  // bytes; an FP8 pool (quantise-on-store) or other rows take a store launch first
+  const int E = pool.dtype == PA_F32 ? 4 : 2;
+  auto al = [&](const void* p, int64_t st, int64_t sh) {
+    return ((uintptr_t)p & 15u) == 0 && (st * E) % 16 == 0 && (sh * E) % 16 == 0;
+  };
+  const bool foldable = pool.dtype != PA_FP8_E4M3 && rows.src_dtype == pool.dtype &&
+                        al(rows.k, rows.k_st, rows.k_sh) && al(rows.v, rows.v_st, rows.v_sh);
+  if (!foldable) {
+    const int st = launch_store(pool, rows.k, rows.v, rows.src_dtype, a.num_seqs, rows.k_st,
+                                rows.k_sh, rows.v_st, rows.v_sh, rows.slots, stream);
+    if (st != PA_OK) return st;
+    return dispatch(pool, a, nullptr, stream);
+  }
+  return dispatch(pool, a, &rows, stream);
 }
 
 }  // namespace pa

@@ -41,6 +41,20 @@ constexpr size_t kDecodeCounterBytes = kDecodeCounters * sizeof(unsigned);
 
 int launch_decode(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream);
 
+// New rows of a decode step: row s of k / v ([num_seqs, kv_heads, head_dim] of src_dtype,
+// element strides) is sequence s's newest token, to be stored at slots[s] (< 0: none).
+struct StepRows {
+  const void* k;
+  const void* v;
+  int src_dtype;
+  int64_t k_st, k_sh, v_st, v_sh;
+  const int64_t* slots;
+};
+
+// Store the step's rows, then decode; one launch when the single-launch schedule runs.
+int launch_decode_step(const pa_kv_pool_t& pool, const DecodeArgs& a, const StepRows& rows,
+                       hipStream_t stream);
+
 struct PrefillArgs {
   void* out;
   int64_t out_st, out_sh;

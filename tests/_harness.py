@@ -23,9 +23,10 @@ def to_dev(x, dtype, dev):
 
 
 class Setup:
-    """Device and oracle state of one case after this step's store."""
+    """Device and oracle state of one case after this step's store (the oracle side
+    always includes it; store_new=False leaves the device store to the test)."""
 
-    def __init__(self, case, dev, poison=True, split_tokens=0):
+    def __init__(self, case, dev, poison=True, split_tokens=0, store_new=True):
         self.case, self.dev = case, dev
         self.split_tokens = split_tokens
         c = case
@@ -47,7 +48,8 @@ class Setup:
                                        c.slot_mapping)
             self.ref_v = ref.store_ref(vp.astype(np.float64), c.v_new.astype(np.float64),
                                        c.slot_mapping)
-        pa.store_kv(self.pool, self.k_new, self.v_new, self.slots)
+        if store_new:   # else the caller stores this step's rows (e.g. decode_step)
+            pa.store_kv(self.pool, self.k_new, self.v_new, self.slots)
 
     def _setup_fp8(self, poison):
         c, dev = self.case, self.dev

@@ -29,7 +29,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared()
-    assert set(names) >= {"pa_store_kv", "pa_decode", "pa_varlen_prefill",
+    assert set(names) >= {"pa_store_kv", "pa_decode", "pa_varlen_prefill", "pa_decode_step",
                           "pa_decode_workspace_bytes", "pa_status_string",
                           "pa_decode_default_split_tokens", "pa_varlen_prefill_workspace_bytes"}
     for n in names:
@@ -104,6 +104,27 @@ def test_decode_validation(lib):
     assert need == 4096 + 2 * 12 * 8 * 129 * 4          # counters, then partials
     assert decode(lib, p, split=16, ws=0xC000, wsb=need - 1) == WORKSPACE
     assert decode(lib, p, split=16, ws=0xC008, wsb=need) == WORKSPACE    # not 16-B aligned
+
+
+def step(lib, pool, src=pa.PA_BF16, B=2, k=0xC000, v=0xD000, sm=0xE000, kst=256, ws=0, wsb=0):
+    return lib.pa_decode_step(0x8000, 1536, 128, 0x9000, 1536, 128, pa.PA_BF16, B, 12,
+                              ctypes.byref(pool), k, v, src, kst, 128, kst, 128, sm, 0xA000, 8,
+                              0xB000, 128, 0.1, 128, ws, wsb, None)   # one split: no workspace
+
+
+def test_decode_step_validation(lib):
+    p = fake_pool()
+    assert step(lib, p, B=0) == OK
+    assert step(lib, p, B=-1) == INVALID
+    assert step(lib, p, src=pa.PA_F32) == INVALID             # rows must match a bf16 pool
+    assert step(lib, p, k=0) == INVALID
+    assert step(lib, p, sm=0) == INVALID
+    assert step(lib, p, kst=-1) == INVALID
+    fp8 = fake_pool(pa.PA_FP8_E4M3, scales=True)
+    assert lib.pa_decode_step(0x8000, 1536, 128, 0x9000, 1536, 128, pa.PA_BF16, 2, 12,
+                              ctypes.byref(fp8), 0xC000, 0xD000, pa.PA_FP8_E4M3, 256, 128, 256,
+                              128, 0xE000, 0xA000, 8, 0xB000, 128, 0.1, 128, 0, 0,
+                              None) == INVALID               # FP8 pools take bf16/f32 rows
 
 
 def test_default_split_and_workspace_bytes(lib):
