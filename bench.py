@@ -15,8 +15,8 @@ touched per step) keeps the decode reads from being served by the 256 MB MALL.
 Prints one JSON line: value = algorithmic KV + query/output bytes moved per step /
 step time (GB/s), with seqs/s, the decode kernel's roofline (HIP-event timed average
 launch over a graph of decode launches only), the CPU oracle's rate on a bounded sample
-and, unless --no-extra, the same figures for the 256-sequence decode, the FP8 decode
-and the varlen prefill.
+and, unless --no-extra, the same figures for the 256-sequence decode, the FP8 and INT8
+decodes and the varlen prefill.
 """
 import argparse
 import json
@@ -230,9 +230,9 @@ def extra_large_decode(torch, pa, W, dev, reps=20, split_tokens=0):
             "seqs_per_s": round(case.num_seqs / ((ms + ms_store) / 1e3), 1)}
 
 
-def extra_fp8_decode(torch, pa, W, dev, reps=30, copies=2, split_tokens=0):
-    """Two copies of the 64 x 8192 FP8 multi-slot pool (277 MB each) alternate, so a call
-    does not find its pool in the MALL left by the previous one."""
+def extra_fp8_decode(torch, pa, W, dev, reps=30, copies=2, split_tokens=0, dtype="fp8"):
+    """Two copies of the 64 x 8192 FP8 (or INT8) multi-slot pool (277 MB each) alternate,
+    so a call does not find its pool in the MALL left by the previous one."""
     case = W.make(5)
     ctx_len = case.extra["ctx"]
     B, hkv, D = case.num_seqs, case.Hkv, case.D
@@ -242,7 +242,7 @@ def extra_fp8_decode(torch, pa, W, dev, reps=30, copies=2, split_tokens=0):
     src = torch.empty((B * (ctx_len - 1), hkv, D), dtype=torch.bfloat16, device=dev)
     pools = []
     for c in range(copies):
-        pool = pa.KVPool.empty(case.num_blocks, hkv, D, "fp8", dev)
+        pool = pa.KVPool.empty(case.num_blocks, hkv, D, dtype, dev)
         W.fill_device_normal_(src, case.seed * 1000 + 1 + 10 * c)
         srcv = src.clone()
         W.fill_device_normal_(srcv, case.seed * 1000 + 2 + 10 * c)
@@ -271,7 +271,8 @@ def extra_fp8_decode(torch, pa, W, dev, reps=30, copies=2, split_tokens=0):
     ms = time_graph(torch, g, reps) / copies
     ms_store = time_graph(torch, gs, reps) / copies
     by = decode_bytes(case.context_lens, case.Hq, hkv, D, 1, fp8_scales=True)
-    return {"workload": "64 x 8192 FP8 e4m3 decode, 12/2 heads, D 128, per-token-head fp32 "
+    name = "FP8 e4m3" if dtype == "fp8" else "INT8"
+    return {"workload": f"64 x 8192 {name} decode, 12/2 heads, D 128, per-token-head fp32 "
                         "scales, multi-slot layout viewed as 16-token blocks",
             "decode_ms": round(ms, 4), "store_ms": round(ms_store, 4), "kv_bytes": by,
             "gbs": round(by / ms / 1e6, 1),
@@ -410,6 +411,9 @@ def main():
         torch.cuda.empty_cache()
         log("extra: fp8 decode")
         res["extra"]["fp8_decode"] = extra_fp8_decode(torch, pa, W, dev)
+        torch.cuda.empty_cache()
+        log("extra: int8 decode")
+        res["extra"]["int8_decode"] = extra_fp8_decode(torch, pa, W, dev, dtype="int8")
         torch.cuda.empty_cache()
         log("extra: varlen prefill")
         res["extra"]["varlen_prefill"] = extra_prefill(torch, pa, W, dev)

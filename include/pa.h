@@ -48,7 +48,7 @@
  *    tokens of the current step, which must be stored before attention runs ([P4]
  *    "errors, type 1": a context length one short hides the new token from itself).
  *  - Supported: block_size 16; head_dim 64 or 128; q_heads / kv_heads in 1..8.
- *    dtypes: (q F32, pool F32), (q BF16, pool BF16), (q BF16, pool FP8_E4M3).
+ *    dtypes: (q F32, pool F32), (q BF16, pool BF16), (q BF16, pool FP8_E4M3 or INT8).
  *  - Validation happens on the host before any launch; a failing call launches
  *    nothing and returns a negative status. Device-data preconditions (block ids in
  *    range, 1 <= context_lens[s] <= max_context_len, n_s <= context_lens[s]) are the
@@ -71,7 +71,8 @@ extern "C" {
 enum {
   PA_F32 = 0,      /* IEEE binary32 */
   PA_BF16 = 1,     /* bfloat16 */
-  PA_FP8_E4M3 = 2  /* OCP e4m3fn codes (bias 7, max 448, no infinities), KV pools only */
+  PA_FP8_E4M3 = 2, /* OCP e4m3fn codes (bias 7, max 448, no infinities), KV pools only */
+  PA_INT8 = 3      /* symmetric int8 codes in [-127, 127], KV pools only */
 };
 
 /* Status codes. */
@@ -86,7 +87,7 @@ enum {
 /* One layer's KV pool. Caller-owned, dense, persists across calls (it is the cache).
  *   k, v       [num_blocks, block_size, kv_heads, head_dim] of `dtype`
  *   k_scale,   [num_blocks, block_size, kv_heads] fp32; required iff dtype is
- *   v_scale    PA_FP8_E4M3 (per-token-per-head dequantisation scales, the
+ *   v_scale    PA_FP8_E4M3 or PA_INT8 (per-token-per-head dequantisation scales, the
  *              k_scale/v_scale "used for FP8/INT8 quantisation" of [P2]), else NULL. */
 typedef struct pa_kv_pool {
   void *k;
@@ -125,6 +126,9 @@ const char *pa_status_string(int status);
  *         code_d = e4m3fn(x_d / scale) with round-to-nearest-even and saturation to
  *         +-448; a == 0 gives scale 0 and all codes 0x00. Codes go to the pool, the
  *         scale to pool->k_scale[slot / block_size][slot % block_size][g] (same for v).
+ *     pool->dtype == PA_INT8 (src_dtype F32 or BF16): the same with 127 in place of 448
+ *         and code_d = x_d / scale rounded to the nearest integer, ties to even,
+ *         clamped to [-127, 127] (two's complement bytes).
  *         Source values must be finite.
  *   Every byte of the pool not named by a valid slot is left untouched.
  *   num_tokens == 0 is a no-op returning PA_OK.
@@ -161,7 +165,8 @@ int32_t pa_decode_default_split_tokens(int32_t num_seqs, int32_t kv_heads,
  * context_lens counts. For sequence s, query head h, g = h / (q_heads/kv_heads),
  * L = context_lens[s]:
  *     out[s][h][:] = sum_{j<L} softmax_j(scale * q[s][h] . K_s[j][g]) * V_s[j][g][:]
- * where K_s[j] is the pool row at slot(s, j). FP8 pools dequantise as code * scale.
+ * where K_s[j] is the pool row at slot(s, j). FP8 and INT8 pools dequantise as
+ * code * scale.
  *
  *   out          [num_seqs, q_heads, head_dim] of q_dtype, strides (out_stride_tok,
  *                out_stride_head); every element is written exactly once.

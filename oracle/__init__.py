@@ -9,6 +9,8 @@ Modules
   fp8    OCP e4m3fn codec written from the format definition (decode table, nearest-
          value encoder with ties to even and saturation) and the per-token-per-head
          absmax/448 quantiser.
+  int8   symmetric int8 codec: absmax/127 per-token-per-head quantiser (nearest
+         integer, ties to even, clamp to [-127, 127]) and its dequantisation.
   ref    the plain definition: store through slot_mapping, gather the paged KV of each
          sequence through its block table, then dense causal softmax attention; also
          partial (lse, o) over a key subset and their log-sum-exp merge.

@@ -81,6 +81,21 @@ def store_fp8_ref(codes, scales, src_f32, slot_mapping):
     return c_out, s_out
 
 
+def store_int8_ref(codes, scales, src_f32, slot_mapping):
+    """INT8 store: as store_fp8_ref with oracle.int8.quantize_rows. codes: int8
+    [nb, bs, Hkv, D]; scales: float32 [nb, bs, Hkv]. Returns copies."""
+    from . import int8
+    c_out, s_out = codes.copy(), scales.copy()
+    q_codes, q_scale = int8.quantize_rows(src_f32)
+    nb, bs = codes.shape[0], codes.shape[1]
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0 or slot >= nb * bs:
+            continue
+        c_out[slot // bs, slot % bs] = q_codes[t]
+        s_out[slot // bs, slot % bs] = q_scale[t]
+    return c_out, s_out
+
+
 # ----------------------------------------------------------------------------- gather
 
 def gather_seq(pool_vals, block_table_row, length):

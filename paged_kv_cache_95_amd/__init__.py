@@ -19,13 +19,16 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
-PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
 PA_OK = 0
 BLOCK_SIZE = 16
 
-_DTYPE_CODE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3}
-_NAME_CODE = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
-_NAME_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+_DTYPE_CODE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
+               torch.int8: PA_INT8}
+_NAME_CODE = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3, "int8": PA_INT8}
+_NAME_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
+               "int8": torch.int8}
+_QUANT = (PA_FP8_E4M3, PA_INT8)
 
 
 class PaError(RuntimeError):
@@ -110,7 +113,7 @@ def _need(cond, msg):
 
 class KVPool:
     """One layer's paged KV cache: k, v [num_blocks, 16, kv_heads, head_dim] (bf16,
-    fp32, or uint8 e4m3fn codes) and, for FP8, fp32 k_scale/v_scale
+    fp32, uint8 e4m3fn codes or int8 codes) and, for FP8 / INT8, fp32 k_scale/v_scale
     [num_blocks, 16, kv_heads]. Tensors are owned by the caller (this object)."""
 
     def __init__(self, k, v, k_scale=None, v_scale=None, dtype=None):
@@ -118,8 +121,8 @@ class KVPool:
         _need(k.is_contiguous() and v.is_contiguous(), "pools must be dense")
         self.k, self.v, self.k_scale, self.v_scale = k, v, k_scale, v_scale
         self.dtype = _DTYPE_CODE[k.dtype] if dtype is None else _NAME_CODE[dtype]
-        if self.dtype == PA_FP8_E4M3:
-            _need(k_scale is not None and v_scale is not None, "FP8 pool needs scales")
+        if self.dtype in _QUANT:
+            _need(k_scale is not None and v_scale is not None, "FP8/INT8 pool needs scales")
             _need(k_scale.dtype == torch.float32 and k_scale.shape == k.shape[:3]
                   and k_scale.is_contiguous() and v_scale.is_contiguous()
                   and v_scale.shape == k.shape[:3], "scales must be fp32 [nb, bs, Hkv]")
@@ -137,7 +140,7 @@ class KVPool:
         k = torch.empty(shape, dtype=td, device=device)
         v = torch.empty(shape, dtype=td, device=device)
         ks = vs = None
-        if dtype == "fp8":
+        if dtype in ("fp8", "int8"):
             ks = torch.empty(shape[:3], dtype=torch.float32, device=device)
             vs = torch.empty(shape[:3], dtype=torch.float32, device=device)
         return cls(k, v, ks, vs, dtype=dtype)

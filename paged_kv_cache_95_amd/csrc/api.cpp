@@ -19,9 +19,10 @@ bool pool_shape_ok(const pa_kv_pool_t* p, int* status) {
   if (!p || !p->k || !p->v) return *status = PA_ERR_INVALID_ARG, false;
   if (p->num_blocks <= 0 || p->block_size <= 0 || p->kv_heads <= 0 || p->head_dim <= 0)
     return *status = PA_ERR_INVALID_ARG, false;
-  if (p->dtype != PA_F32 && p->dtype != PA_BF16 && p->dtype != PA_FP8_E4M3)
+  if (p->dtype != PA_F32 && p->dtype != PA_BF16 && p->dtype != PA_FP8_E4M3 &&
+      p->dtype != PA_INT8)
     return *status = PA_ERR_INVALID_ARG, false;
-  if (p->dtype == PA_FP8_E4M3 && (!p->k_scale || !p->v_scale))
+  if ((p->dtype == PA_FP8_E4M3 || p->dtype == PA_INT8) && (!p->k_scale || !p->v_scale))
     return *status = PA_ERR_INVALID_ARG, false;
   if (p->block_size != kBlockSize) return *status = PA_ERR_UNSUPPORTED, false;
   if (p->head_dim != 64 && p->head_dim != 128) return *status = PA_ERR_UNSUPPORTED, false;
@@ -30,7 +31,8 @@ bool pool_shape_ok(const pa_kv_pool_t* p, int* status) {
 
 bool q_dtype_ok(int q_dtype, int pool_dtype) {
   return (q_dtype == PA_F32 && pool_dtype == PA_F32) ||
-         (q_dtype == PA_BF16 && (pool_dtype == PA_BF16 || pool_dtype == PA_FP8_E4M3));
+         (q_dtype == PA_BF16 &&
+          (pool_dtype == PA_BF16 || pool_dtype == PA_FP8_E4M3 || pool_dtype == PA_INT8));
 }
 
 // Split length used when the caller passes 0: aim at about 2048 (sequence, KV head,
@@ -49,9 +51,9 @@ int effective_split(int split_tokens, int64_t num_seqs, int kv_heads, int max_co
 // Source rows of pa_store_kv / pa_decode_step: dtype pairing and strides.
 int check_store_rows(const pa_kv_pool_t* pool, int32_t src_dtype, int64_t k_stride_tok,
                      int64_t k_stride_head, int64_t v_stride_tok, int64_t v_stride_head) {
-  const bool src_ok = pool->dtype == PA_FP8_E4M3
-                          ? (src_dtype == PA_BF16 || src_dtype == PA_F32)
-                          : src_dtype == pool->dtype;
+  const bool quant = pool->dtype == PA_FP8_E4M3 || pool->dtype == PA_INT8;
+  const bool src_ok = quant ? (src_dtype == PA_BF16 || src_dtype == PA_F32)
+                            : src_dtype == pool->dtype;
   if (!src_ok) return PA_ERR_INVALID_ARG;
   if (k_stride_tok < 0 || k_stride_head < 0 || v_stride_tok < 0 || v_stride_head < 0)
     return PA_ERR_INVALID_ARG;

@@ -13,6 +13,14 @@ namespace pa {
 constexpr int kF32 = PA_F32;
 constexpr int kBF16 = PA_BF16;
 constexpr int kFP8 = PA_FP8_E4M3;
+constexpr int kINT8 = PA_INT8;
+
+// Pools of one-byte codes with per-token-per-head fp32 scales.
+template <int T>
+constexpr bool kQuant = T == kFP8 || T == kINT8;
+// Largest code magnitude: the absmax of a row maps to it.
+template <int T>
+constexpr float kQMax = T == kFP8 ? 448.0f : 127.0f;
 
 template <int T>
 struct ElemBytes;
@@ -22,6 +30,8 @@ template <>
 struct ElemBytes<kBF16> { static constexpr int value = 2; };
 template <>
 struct ElemBytes<kFP8> { static constexpr int value = 1; };
+template <>
+struct ElemBytes<kINT8> { static constexpr int value = 1; };
 
 // ------------------------------------------------------------------ bf16 <-> f32
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -86,10 +96,42 @@ __device__ __forceinline__ bf2 bf16x2_rne(float lo, float hi) {
   return __builtin_convertvector(x, bf2);
 }
 
+// ------------------------------------------------------------------ symmetric int8
+// Round to nearest even and clamp to [-127, 127]; the code as its two's complement byte.
+__device__ __forceinline__ uint32_t f32_to_i8sym(float y) {
+  const float r = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
+  return (uint32_t)(int32_t)r & 0xffu;
+}
+
+// Bytes 0,1 (or 2,3) of w as signed codes -> two fp32 values (exact).
+__device__ __forceinline__ void i8x2_to_f32(uint32_t w, bool high, float& a, float& b) {
+  const int32_t x = (int32_t)(high ? w : w << 16);
+  a = (float)((x << 8) >> 24);
+  b = (float)(x >> 24);
+}
+
 // Pack the bf16 images of two fp32 values that are exactly representable in bf16
 // (low half = lo, high half = hi).
 __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Two one-byte codes of a quantised pool -> fp32 values / their bf16 pair (exact:
+// every e4m3fn value and every integer in [-127, 127] is a bf16 value).
+template <int KVT>
+__device__ __forceinline__ void q8x2_to_f32(uint32_t w, bool high, float& a, float& b) {
+  if constexpr (KVT == kFP8) e4m3x2_to_f32(w, high, a, b);
+  else i8x2_to_f32(w, high, a, b);
+}
+template <int KVT>
+__device__ __forceinline__ uint32_t q8x2_to_bf16x2(uint32_t w, bool high) {
+  if constexpr (KVT == kFP8) {
+    return e4m3x2_to_bf16x2(w, high);
+  } else {
+    float a, b;
+    i8x2_to_f32(w, high, a, b);
+    return pack_bf16_exact(a, b);
+  }
 }
 
 // ------------------------------------------------------------------ streaming loads

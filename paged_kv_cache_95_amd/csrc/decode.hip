@@ -83,7 +83,7 @@ struct BlockBuf {
 // wave per SIMD (an FP8 block buffer is half the size of a bf16 one).
 template <int KVT, int G>
 struct RingDepth {
-  static constexpr int value = KVT == kFP8 ? (G <= 4 ? 4 : (G <= 6 ? 3 : 2)) : (G <= 4 ? 3 : 2);
+  static constexpr int value = kQuant<KVT> ? (G <= 4 ? 4 : (G <= 6 ? 3 : 2)) : (G <= 4 ? 3 : 2);
 };
 
 template <int KVT, int D, int G>
@@ -116,11 +116,11 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
           s[k][h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][w]),
                                                     __builtin_bit_cast(bf2, b.k[k][w]), s[k][h],
                                                     false);
-    } else if constexpr (KVT == kFP8) {
+    } else if constexpr (kQuant<KVT>) {
 #pragma unroll
       for (int w = 0; w < Gm::KC * 4; ++w) {
-        const uint32_t p0 = e4m3x2_to_bf16x2(b.k[k][w], false);
-        const uint32_t p1 = e4m3x2_to_bf16x2(b.k[k][w], true);
+        const uint32_t p0 = q8x2_to_bf16x2<KVT>(b.k[k][w], false);
+        const uint32_t p1 = q8x2_to_bf16x2<KVT>(b.k[k][w], true);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           s[k][h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][2 * w]),
@@ -150,7 +150,7 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
       y += dpp<kQuadXor1>(y);
       y += dpp<kQuadXor2>(y);
       y += dpp<kHalfMirror>(y);
-      y *= KVT == kFP8 ? scale_log2 * b.ks[k] : scale_log2;
+      y *= kQuant<KVT> ? scale_log2 * b.ks[k] : scale_log2;
       x[k] = MASKED ? (valid_k[k] ? y : NEG_INF) : y;
     }
     float mb = fmaxf(x[0], x[1]);
@@ -177,7 +177,7 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
       for (int e = 0; e < Gm::EV; ++e) st.acc[h][e] *= alpha;
     }
   }
-  if constexpr (KVT == kFP8) {
+  if constexpr (kQuant<KVT>) {
     // fold the V scale of each token into its probability (the mirror delivers the
     // other half-row's already scaled values); invalid tokens stay exactly 0
 #pragma unroll
@@ -189,9 +189,9 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
       }
   }
   // ---- V: the row's four tokens (own set 0, other set 0, own set 1, other set 1)
-  if constexpr (KVT == kFP8) {
+  if constexpr (kQuant<KVT>) {
     // Token pairs (own, other) of each set: per head dim, the two tokens' values form
-    // one bf16 pair (FP8 codes are exact in bf16), the two probabilities another
+    // one bf16 pair (the codes are exact in bf16), the two probabilities another
     // (rounded once to bf16), and one dot2 does both multiply-adds in fp32.
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -202,10 +202,10 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
       for (int w = 0; w < Gm::VW; ++w) {
         const uint32_t ya = ok_a ? b.v[2 * k][w] : 0u;  // invalid tokens: exact zeros
         const uint32_t yb = ok_b ? b.v[2 * k + 1][w] : 0u;
-        e4m3x2_to_f32(ya, false, va[4 * w], va[4 * w + 1]);
-        e4m3x2_to_f32(ya, true, va[4 * w + 2], va[4 * w + 3]);
-        e4m3x2_to_f32(yb, false, vb[4 * w], vb[4 * w + 1]);
-        e4m3x2_to_f32(yb, true, vb[4 * w + 2], vb[4 * w + 3]);
+        q8x2_to_f32<KVT>(ya, false, va[4 * w], va[4 * w + 1]);
+        q8x2_to_f32<KVT>(ya, true, va[4 * w + 2], va[4 * w + 3]);
+        q8x2_to_f32<KVT>(yb, false, vb[4 * w], vb[4 * w + 1]);
+        q8x2_to_f32<KVT>(yb, true, vb[4 * w + 2], vb[4 * w + 3]);
       }
       uint32_t vp[Gm::EV];
 #pragma unroll
@@ -421,7 +421,7 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
 #pragma unroll
     for (int x = 0; x < 4; ++x)
       load_dwords<Gm::VW>(tok_v[x] == pnew ? vrow_new + cv * Gm::VB : vb + vofs[x], b.v[x]);
-    if constexpr (KVT == kFP8) {
+    if constexpr (kQuant<KVT>) {
       const int64_t sb = bid * kBlockSize * a.hkv;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -1049,6 +1049,9 @@ static int dispatch(const pa_kv_pool_t& pool, const DecodeArgs& a, const StepRow
     case PA_FP8_E4M3:
       return D == 64 ? dispatch_g<kFP8, 64, kBF16>(pool, a, step, stream)
                      : dispatch_g<kFP8, 128, kBF16>(pool, a, step, stream);
+    case PA_INT8:
+      return D == 64 ? dispatch_g<kINT8, 64, kBF16>(pool, a, step, stream)
+                     : dispatch_g<kINT8, 128, kBF16>(pool, a, step, stream);
     default:
       return PA_ERR_UNSUPPORTED;
   }
@@ -1061,12 +1064,13 @@ int launch_decode(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t str
 int launch_decode_step(const pa_kv_pool_t& pool, const DecodeArgs& a, const StepRows& rows,
                        hipStream_t stream) {
   // the store folds into the single-launch kernel for same-dtype rows that start on 16
-  // bytes; an FP8 pool (quantise-on-store) or other rows take a store launch first
+  // bytes; a quantised pool (quantise-on-store) or other rows take a store launch first
   const int E = pool.dtype == PA_F32 ? 4 : 2;
   auto al = [&](const void* p, int64_t st, int64_t sh) {
     return ((uintptr_t)p & 15u) == 0 && (st * E) % 16 == 0 && (sh * E) % 16 == 0;
   };
-  const bool foldable = pool.dtype != PA_FP8_E4M3 && rows.src_dtype == pool.dtype &&
+  const bool foldable = pool.dtype != PA_FP8_E4M3 && pool.dtype != PA_INT8 &&
+                        rows.src_dtype == pool.dtype &&
                         al(rows.k, rows.k_st, rows.k_sh) && al(rows.v, rows.v_st, rows.v_sh);
   if (!foldable) {
     const int st = launch_store(pool, rows.k, rows.v, rows.src_dtype, a.num_seqs, rows.k_st,

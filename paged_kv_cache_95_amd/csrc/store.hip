@@ -3,8 +3,9 @@
 // Follows the store_kvcache_kernel of the koas-w "errors and solutions" post
 // ("hand-written Triton kernels": token x head grid, rows written straight to their
 // physical slot, strides for non-contiguous inputs) and the per-slot append of
-// PocketLLM "cpp_engine Batching Implementation (Phase 3.1)" (Step 3.4). The FP8
-// variant adds the per-token-per-head absmax/448 quantiser.
+// PocketLLM "cpp_engine Batching Implementation (Phase 3.1)" (Step 3.4). The FP8 and
+// INT8 variants add the per-token-per-head absmax quantiser (the k_scale / v_scale that
+// page lists "for FP8/INT8").
 //
 // Layout: pool [num_blocks, 16, Hkv, D]; the row of (slot, g) starts at element
 // (slot * Hkv + g) * D, because block * 16 + offset == slot.
@@ -47,12 +48,14 @@ __global__ void __launch_bounds__(256) store_copy_kernel(
   }
 }
 
-// ---------------------------------------------------------------- FP8 quantise + store
+// ---------------------------------------------------------------- quantise + store
 // 16 lanes per (k|v, token, head) row, EPL = D/16 elements per lane; 16 rows per
-// 256-thread block. absmax over the row via the 16-lane butterfly, scale = a / 448
-// (correctly rounded fp32 divide), codes = e4m3fn(x / scale).
-template <int SRC, int D>
-__global__ void __launch_bounds__(256) store_fp8_kernel(
+// 256-thread block. absmax over the row via the 16-lane butterfly, scale = a / QMAX
+// (correctly rounded fp32 divide; 448 for e4m3fn, 127 for int8), codes = the pool's
+// encoding of x / scale (e4m3fn: round to nearest even with saturation; int8: nearest
+// integer, ties to even, clamped to [-127, 127]).
+template <int SRC, int D, int Q>
+__global__ void __launch_bounds__(256) store_quant_kernel(
     uint8_t* __restrict__ kpool, uint8_t* __restrict__ vpool, float* __restrict__ kscale,
     float* __restrict__ vscale, const void* __restrict__ ksrc, const void* __restrict__ vsrc,
     int64_t k_st, int64_t k_sh, int64_t v_st, int64_t v_sh,
@@ -87,14 +90,18 @@ __global__ void __launch_bounds__(256) store_fp8_kernel(
     for (int e = 0; e < EPL; ++e) a = fmaxf(a, fabsf(x[e]));
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, 16));
-    const float scale = a / 448.0f;
+    const float scale = a / kQMax<Q>;
     uint32_t words[EPL / 4];
 #pragma unroll
     for (int w = 0; w < EPL / 4; ++w) {
       uint32_t word = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const uint32_t code = (a == 0.0f) ? 0u : f32_to_e4m3fn(x[4 * w + b] / scale);
+        uint32_t code = 0u;
+        if (a != 0.0f) {
+          const float y = x[4 * w + b] / scale;
+          code = Q == kFP8 ? f32_to_e4m3fn(y) : f32_to_i8sym(y);
+        }
         word |= code << (8 * b);
       }
       words[w] = word;
@@ -122,18 +129,25 @@ int launch_store(const pa_kv_pool_t& pool, const void* k, const void* v, int src
                  const int64_t* slot_mapping, hipStream_t stream) {
   const int64_t num_slots = pool.num_blocks * pool.block_size;
   const int hkv = pool.kv_heads, D = pool.head_dim;
-  if (pool.dtype == PA_FP8_E4M3) {
+  if (pool.dtype == PA_FP8_E4M3 || pool.dtype == PA_INT8) {
     const int grid = grid_for(2 * num_tokens * hkv * 16, 256);
-#define PA_FP8_STORE(SRC, DD)                                                               \
-  store_fp8_kernel<SRC, DD><<<grid, 256, 0, stream>>>(                                     \
+#define PA_QUANT_STORE(SRC, DD, Q)                                                          \
+  store_quant_kernel<SRC, DD, Q><<<grid, 256, 0, stream>>>(                                \
       (uint8_t*)pool.k, (uint8_t*)pool.v, pool.k_scale, pool.v_scale, k, v, k_st, k_sh,    \
       v_st, v_sh, slot_mapping, num_tokens, hkv, num_slots)
-    if (src_dtype == PA_BF16 && D == 128) PA_FP8_STORE(kBF16, 128);
-    else if (src_dtype == PA_BF16 && D == 64) PA_FP8_STORE(kBF16, 64);
-    else if (src_dtype == PA_F32 && D == 128) PA_FP8_STORE(kF32, 128);
-    else if (src_dtype == PA_F32 && D == 64) PA_FP8_STORE(kF32, 64);
+#define PA_QUANT_STORE_Q(Q)                                                                 \
+    if (src_dtype == PA_BF16 && D == 128) PA_QUANT_STORE(kBF16, 128, Q);                    \
+    else if (src_dtype == PA_BF16 && D == 64) PA_QUANT_STORE(kBF16, 64, Q);                 \
+    else if (src_dtype == PA_F32 && D == 128) PA_QUANT_STORE(kF32, 128, Q);                 \
+    else if (src_dtype == PA_F32 && D == 64) PA_QUANT_STORE(kF32, 64, Q);                   \
     else return PA_ERR_UNSUPPORTED;
-#undef PA_FP8_STORE
+    if (pool.dtype == PA_FP8_E4M3) {
+      PA_QUANT_STORE_Q(kFP8)
+    } else {
+      PA_QUANT_STORE_Q(kINT8)
+    }
+#undef PA_QUANT_STORE_Q
+#undef PA_QUANT_STORE
     return PA_OK;
   }
   const int E = pool.dtype == PA_F32 ? 4 : 2;

@@ -2,8 +2,9 @@
 run the HIP path through the binding, and run the oracle on the same inputs.
 
 The oracle side never sees a value produced by the HIP path: bf16/fp32 pools start from
-the generator's values and get the new rows via oracle.ref.store_ref; FP8 pools are
-filled by oracle.ref.store_fp8_ref from the same bf16 source the GPU store consumes.
+the generator's values and get the new rows via oracle.ref.store_ref; FP8 / INT8 pools
+are filled by oracle.ref.store_fp8_ref / store_int8_ref from the same bf16 source the
+GPU store consumes.
 """
 import numpy as np
 import torch
@@ -11,9 +12,12 @@ import torch
 import paged_kv_cache_95_amd as pa
 import workloads as W
 from oracle import fp8 as ofp8
+from oracle import int8 as oint8
 from oracle import ref
 
-TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 3e-2}
+# INT8 pools run the FP8 arithmetic (codes exact in bf16, probabilities rounded once
+# to bf16 for P.V), so they take the FP8 bound.
+TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 3e-2, "int8": 3e-2}
 NAN_CODE = 0x7F  # e4m3fn NaN pattern, used to poison unused FP8 slots
 
 
@@ -38,8 +42,8 @@ class Setup:
         self.v_new = to_dev(c.v_new, td, dev)
         self.slots = torch.from_numpy(c.slot_mapping).to(dev)
         self.cu = torch.from_numpy(c.cu_seqlens).to(dev) if c.cu_seqlens is not None else None
-        if c.kv_dtype == "fp8":
-            self._setup_fp8(poison)
+        if c.kv_dtype in ("fp8", "int8"):
+            self._setup_quant(poison)
         else:
             kp = W.host_pool(c, "k", poison)
             vp = W.host_pool(c, "v", poison)
@@ -51,12 +55,15 @@ class Setup:
         if store_new:   # else the caller stores this step's rows (e.g. decode_step)
             pa.store_kv(self.pool, self.k_new, self.v_new, self.slots)
 
-    def _setup_fp8(self, poison):
+    def _setup_quant(self, poison):
         c, dev = self.case, self.dev
+        int8 = c.kv_dtype == "int8"
         shape = (c.num_blocks, c.block_size, c.Hkv, c.D)
-        fill = NAN_CODE if poison else 0
-        codes_k = np.full(shape, fill, np.uint8)
-        codes_v = np.full(shape, fill, np.uint8)
+        # unused slots: NaN codes for FP8; INT8 has none, so a garbage code with a NaN
+        # scale (the scales carry the poison there)
+        fill = (-77 if int8 else NAN_CODE) if poison else 0
+        codes_k = np.full(shape, fill, np.int8 if int8 else np.uint8)
+        codes_v = np.full(shape, fill, np.int8 if int8 else np.uint8)
         sk = np.full(shape[:3], np.nan if poison else 0, np.float32)
         sv = sk.copy()
         self.pool = pa.KVPool(torch.from_numpy(codes_k).to(dev), torch.from_numpy(codes_v).to(dev),
@@ -67,16 +74,18 @@ class Setup:
             pa.store_kv(self.pool, to_dev(pk, torch.bfloat16, dev), to_dev(pv, torch.bfloat16, dev),
                         torch.from_numpy(pslots).to(dev))
         all_slots = np.concatenate([pslots, c.slot_mapping])
-        ck, sk2 = ref.store_fp8_ref(codes_k, sk, np.concatenate([pk, c.k_new]), all_slots)
-        cv, sv2 = ref.store_fp8_ref(codes_v, sv, np.concatenate([pv, c.v_new]), all_slots)
+        store = ref.store_int8_ref if int8 else ref.store_fp8_ref
+        ck, sk2 = store(codes_k, sk, np.concatenate([pk, c.k_new]), all_slots)
+        cv, sv2 = store(codes_v, sv, np.concatenate([pv, c.v_new]), all_slots)
         self.ref_codes = (ck, sk2, cv, sv2)
-        self.ref_k = self._dequant(ck, sk2)
-        self.ref_v = self._dequant(cv, sv2)
+        self.ref_k = self._dequant(ck, sk2, int8)
+        self.ref_v = self._dequant(cv, sv2, int8)
 
     @staticmethod
-    def _dequant(codes, scales):
-        vals = ofp8.decode(codes) * scales.astype(np.float64)[..., None]
-        return vals
+    def _dequant(codes, scales, int8=False):
+        if int8:
+            return oint8.dequantize(codes, scales)
+        return ofp8.decode(codes) * scales.astype(np.float64)[..., None]
 
     # ------------------------------------------------------------------ runs
     def gpu(self, **kw):

@@ -36,7 +36,7 @@ def test_qwen_decode_bf16(dev):
         check(s, split_tokens=split)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "f32", "fp8", "int8"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 6, 8])
 def test_random_shapes(dev, kv, D, G):
@@ -82,7 +82,7 @@ def _permuted(setup_a, case, dev, perm):
     return case2, pool2
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
 def test_block_permutation_is_bit_identical(dev, kv):
     case = W.random_case(9, B=6, Hq=12, Hkv=2, D=128, kv_dtype=kv, lmin=20, lmax=900)
     s = Setup(case, dev)

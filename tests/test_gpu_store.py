@@ -1,4 +1,5 @@
-"""pa_store_kv on the GPU against oracle.ref.store_ref / store_fp8_ref: bit-exact."""
+"""pa_store_kv on the GPU against oracle.ref.store_ref / store_fp8_ref / store_int8_ref:
+bit-exact."""
 import numpy as np
 import pytest
 import torch
@@ -112,3 +113,43 @@ def test_store_fp8_bitexact(dev, D, src):
     assert np.array_equal(pool.k_scale.cpu().numpy().view(np.uint32), sk.view(np.uint32))
     assert np.array_equal(pool.v.cpu().numpy(), cv)
     assert np.array_equal(pool.v_scale.cpu().numpy().view(np.uint32), sv.view(np.uint32))
+
+
+@pytest.mark.parametrize("D,src", [(128, "bf16"), (64, "bf16"), (128, "f32")])
+def test_store_int8_bitexact(dev, D, src):
+    rng = np.random.default_rng(100 + D)
+    T, hkv, nb = 300, 2, 40
+    x = rng.standard_normal((T, hkv, D)).astype(np.float32) * rng.uniform(
+        1e-3, 1e3, size=(T, hkv, 1)).astype(np.float32)
+    x[5, 0] = 0.0                                        # zero row -> scale 0, codes 0
+    x[6, 1] = 0.0
+    x[6, 1, 3] = -2.5                                    # single non-zero -> -127
+    x[7, 0] = 0.0                                        # max 127: scale 1, exact ties
+    x[7, 0, :8] = [127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5]
+    x[8, 1, :] = 1.0                                     # all equal to the max
+    if src == "bf16":
+        x = W.round_to_bf16(x)
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[::17] = -1
+    pool = pa.KVPool.empty(nb, hkv, D, "int8", dev)
+    for t in (pool.k, pool.v):
+        t.fill_(-77)
+    for t in (pool.k_scale, pool.v_scale):
+        t.fill_(-7.0)
+    td = torch.bfloat16 if src == "bf16" else torch.float32
+    xk = torch.from_numpy(x).to(td).to(dev)
+    xv = torch.from_numpy(-x[::-1].copy()).to(td).to(dev)
+    pa.store_kv(pool, xk, xv, torch.from_numpy(slots).to(dev))
+    torch.cuda.synchronize()
+    c0 = np.full((nb, 16, hkv, D), -77, np.int8)
+    s0 = np.full((nb, 16, hkv), -7.0, np.float32)
+    ck, sk = ref.store_int8_ref(c0, s0, x, slots)
+    cv, sv = ref.store_int8_ref(c0, s0, -x[::-1].copy(), slots)
+    assert np.array_equal(pool.k.cpu().numpy(), ck)
+    assert np.array_equal(pool.k_scale.cpu().numpy().view(np.uint32), sk.view(np.uint32))
+    assert np.array_equal(pool.v.cpu().numpy(), cv)
+    assert np.array_equal(pool.v_scale.cpu().numpy().view(np.uint32), sv.view(np.uint32))
+    # the constructed ties went to even
+    if slots[7] >= 0:
+        row = pool.k.cpu().numpy().reshape(nb * 16, hkv, D)[slots[7], 0, :8]
+        assert row.tolist() == [127, 0, 2, 2, 0, -2, -2, 126]

@@ -51,7 +51,7 @@ def bf16_bits(x):
 
 def normal(rng, shape, dtype):
     x = rng.standard_normal(shape, dtype=np.float32)
-    if dtype == "bf16" or dtype == "fp8":   # fp8 pools are fed from a bf16 source
+    if dtype in ("bf16", "fp8", "int8"):   # quantised pools are fed from a bf16 source
         x = round_to_bf16(x)
     return x
 
@@ -64,7 +64,7 @@ class Case:
     Hq: int
     Hkv: int
     D: int
-    kv_dtype: str                  # "f32", "bf16", "fp8"
+    kv_dtype: str                  # "f32", "bf16", "fp8", "int8"
     q_dtype: str                   # "f32", "bf16"
     num_blocks: int
     block_tables: np.ndarray       # int32 [B, max_blocks_per_seq]; unused entries -1
@@ -101,7 +101,7 @@ class Case:
 
     @property
     def src_dtype(self):
-        return "bf16" if self.kv_dtype == "fp8" else self.kv_dtype
+        return "bf16" if self.kv_dtype in ("fp8", "int8") else self.kv_dtype
 
 
 def _tables_from_perm(perm, lens, max_blocks, bs=BLOCK_SIZE):
@@ -248,7 +248,7 @@ def random_case(seed, kind="decode", B=3, Hq=4, Hkv=2, D=64, kv_dtype="bf16", bs
     perm = rng.permutation(nb).astype(np.int32)
     max_blocks = -(-lmax // bs) + 1
     bt, _ = _tables_from_perm(perm, lens, max_blocks, bs)
-    src = "bf16" if kv_dtype == "fp8" else kv_dtype
+    src = "bf16" if kv_dtype in ("fp8", "int8") else kv_dtype
     qd = "f32" if kv_dtype == "f32" else "bf16"
     if kind == "decode":
         q = normal(rng, (B, Hq, D), qd)
