@@ -5,11 +5,13 @@
  * framework types cross this boundary. Three operations make up the path:
  *
  *   pa_store_kv        write new K/V rows into the paged pool through slot_mapping
- *                      (optionally quantising them to FP8 e4m3 with per-token-per-head
- *                      scales);
+ *                      (optionally quantising them to FP8 e4m3 or INT8 with
+ *                      per-token-per-head scales); pa_rope_store_kv first applies the
+ *                      rotary position embedding to q and k;
  *   pa_decode          one query token per sequence attends its whole cached context,
  *                      read block by block through block_tables, with an online
  *                      softmax; long contexts are split and merged by log-sum-exp;
+ *                      pa_decode_step stores the step's new rows and attends in one;
  *   pa_varlen_prefill  a flat batch of query chunks (cu_seqlens) attends, causally, the
  *                      cached prefix plus the chunk itself, per sequence.
  *
@@ -137,6 +139,49 @@ int pa_store_kv(const pa_kv_pool_t *pool, const void *k, const void *v, int32_t 
                 int64_t num_tokens, int64_t k_stride_tok, int64_t k_stride_head,
                 int64_t v_stride_tok, int64_t v_stride_head, const int64_t *slot_mapping,
                 void *stream);
+
+/*
+ * pa_rope_store_kv - rotary position embedding of a step's new q and k rows, fused with
+ * the store of the rotated k rows and of the v rows into the pool.
+ *
+ * Defined by [P4] "hand-written Triton kernels" (the fused RoPE + KV-cache store: q is
+ * rotated and written back to a contiguous buffer, k and v go straight to their slots
+ * through slot_mapping, no intermediate buffer) with [P4]'s table-driven real-valued
+ * RoPE, numerically aligned with the HuggingFace model (milestone log), whose rotation
+ * pairs dim i with dim i + D/2 of a head.
+ * For token t, position p = positions[t], and each head row x (D = head_dim values) of
+ * q (q_heads rows) and of k (kv_heads rows), with c_i = cos_table[p][i] and
+ * s_i = sin_table[p][i] for i < D/2:
+ *     r_i       = x_i * c_i - x_{i+D/2} * s_i
+ *     r_{i+D/2} = x_{i+D/2} * c_i + x_i * s_i
+ * in fp32 from the exact fp32 values of x, every product and every sum rounded to fp32
+ * on its own (no fused multiply-add).
+ *   q, q_out     [num_tokens, q_heads, head_dim] of src_dtype with element strides;
+ *                q_out receives r rounded once (nearest even) to src_dtype; it may be
+ *                q itself (same pointer and strides).
+ *   k, v         [num_tokens, kv_heads, head_dim] of src_dtype, strided as in
+ *                pa_store_kv. The rotated k rows (fp32 values r) and the v rows are
+ *                stored as pa_store_kv stores rows with those values: rounded to a
+ *                bf16 / fp32 pool (src_dtype must then equal the pool dtype), quantised
+ *                to an FP8 / INT8 pool (with their scales).
+ *   positions    [num_tokens] int64, each in [0, max_position) (an out-of-range value
+ *                leaves that token's rows unspecified; the tables are never read
+ *                outside their bounds).
+ *   cos_table,   fp32 [max_position, head_dim / 2], row-major: the cosine / sine of the
+ *   sin_table    rotation angle of pair i at position p (caller-built, any values).
+ *   slot_mapping [num_tokens] int64; < 0 (or past the pool) stores nothing for that
+ *                token; q is rotated for every token.
+ * num_tokens == 0 is a no-op. Errors as pa_store_kv, plus q_heads not a positive
+ * multiple of kv_heads and max_position <= 0 (PA_ERR_INVALID_ARG).
+ */
+int pa_rope_store_kv(const pa_kv_pool_t *pool, const void *q, int64_t q_stride_tok,
+                     int64_t q_stride_head, int32_t q_heads, void *q_out,
+                     int64_t q_out_stride_tok, int64_t q_out_stride_head, const void *k,
+                     const void *v, int32_t src_dtype, int64_t num_tokens,
+                     int64_t k_stride_tok, int64_t k_stride_head, int64_t v_stride_tok,
+                     int64_t v_stride_head, const int64_t *positions, const float *cos_table,
+                     const float *sin_table, int32_t max_position,
+                     const int64_t *slot_mapping, void *stream);
 
 /*
  * pa_decode_workspace_bytes - bytes of device workspace pa_decode needs for these

@@ -11,6 +11,8 @@ Modules
          absmax/448 quantiser.
   int8   symmetric int8 codec: absmax/127 per-token-per-head quantiser (nearest
          integer, ties to even, clamp to [-127, 127]) and its dequantisation.
+  rope   rotary position embedding (pair i with i + D/2, table-driven, fp32 with every
+         operation rounded) and the fused RoPE + KV store built on ref's stores.
   ref    the plain definition: store through slot_mapping, gather the paged KV of each
          sequence through its block table, then dense causal softmax attention; also
          partial (lse, o) over a key subset and their log-sum-exp merge.

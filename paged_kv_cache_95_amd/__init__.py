@@ -58,6 +58,9 @@ SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32,
                                  ctypes.POINTER(_Pool), _P, _I32, _P, _I32, _F, _I32, _P, _SZ,
                                  _P]),
+    "pa_rope_store_kv": (ctypes.c_int, [ctypes.POINTER(_Pool), _P, _I64, _I64, _I32, _P, _I64,
+                                        _I64, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64, _P,
+                                        _P, _P, _I32, _P, _P]),
     "pa_decode_step": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32,
                                       ctypes.POINTER(_Pool), _P, _P, _I32, _I64, _I64, _I64,
                                       _I64, _P, _P, _I32, _P, _I32, _F, _I32, _P, _SZ, _P]),
@@ -170,6 +173,35 @@ def store_kv(pool, k, v, slot_mapping):
     _check(lib().pa_store_kv(pool.struct, _ptr(k), _ptr(v), _DTYPE_CODE[k.dtype], k.shape[0],
                              ks[0], ks[1], vs[0], vs[1], _ptr(slot_mapping), _stream()),
            "pa_store_kv")
+
+
+def rope_store_kv(pool, q, k, v, positions, cos_table, sin_table, slot_mapping, q_out=None):
+    """Rotary position embedding of q [T, Hq, D] and k [T, kv_heads, D] by the table rows
+    positions [T] (int64) of cos_table / sin_table (fp32 [max_position, D/2]; pair i
+    with i + D/2), fused with the store of the rotated k and of v at slot_mapping [T].
+    Returns the rotated q (q_out, which may be q itself for an in-place rotation)."""
+    qs, ks, vs = _rows3(q, "q"), _rows3(k, "k"), _rows3(v, "v")
+    T = q.shape[0]
+    _need(k.shape == v.shape and k.shape == (T, pool.kv_heads, pool.head_dim), "k/v shape")
+    _need(q.shape[2] == pool.head_dim and q.dtype == k.dtype == v.dtype, "q/k/v dtype or shape")
+    for t, name in ((positions, "positions"), (slot_mapping, "slot_mapping")):
+        _need(t.dtype == torch.int64 and t.dim() == 1 and t.shape[0] == T and t.is_contiguous(),
+              f"{name} must be contiguous int64 [T]")
+    half = pool.head_dim // 2
+    for t, name in ((cos_table, "cos_table"), (sin_table, "sin_table")):
+        _need(t.dtype == torch.float32 and t.dim() == 2 and t.shape[1] == half
+              and t.is_contiguous(), f"{name} must be contiguous fp32 [max_position, D/2]")
+    _need(cos_table.shape == sin_table.shape, "cos/sin tables differ in shape")
+    if q_out is None:
+        q_out = torch.empty((T,) + tuple(q.shape[1:]), dtype=q.dtype, device=q.device)
+    qo = _rows3(q_out, "q_out")
+    _check(lib().pa_rope_store_kv(pool.struct, _ptr(q), qs[0], qs[1], q.shape[1], _ptr(q_out),
+                                  qo[0], qo[1], _ptr(k), _ptr(v), _DTYPE_CODE[k.dtype], T, ks[0],
+                                  ks[1], vs[0], vs[1], _ptr(positions), _ptr(cos_table),
+                                  _ptr(sin_table), cos_table.shape[0], _ptr(slot_mapping),
+                                  _stream()),
+           "pa_rope_store_kv")
+    return q_out
 
 
 def decode_workspace_bytes(num_seqs, q_heads, kv_heads, head_dim, max_context_len,

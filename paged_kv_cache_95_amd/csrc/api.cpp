@@ -87,6 +87,56 @@ int32_t pa_decode_default_split_tokens(int32_t num_seqs, int32_t kv_heads,
 }
 
 
+int pa_rope_store_kv(const pa_kv_pool_t* pool, const void* q, int64_t q_stride_tok,
+                     int64_t q_stride_head, int32_t q_heads, void* q_out,
+                     int64_t q_out_stride_tok, int64_t q_out_stride_head, const void* k,
+                     const void* v, int32_t src_dtype, int64_t num_tokens,
+                     int64_t k_stride_tok, int64_t k_stride_head, int64_t v_stride_tok,
+                     int64_t v_stride_head, const int64_t* positions, const float* cos_table,
+                     const float* sin_table, int32_t max_position,
+                     const int64_t* slot_mapping, void* stream) {
+  int status = PA_OK;
+  if (!pool_shape_ok(pool, &status)) return status;
+  if (num_tokens < 0 || q_heads <= 0 || q_heads % pool->kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (src_dtype != PA_BF16 && src_dtype != PA_F32) return PA_ERR_INVALID_ARG;
+  status = check_store_rows(pool, src_dtype, k_stride_tok, k_stride_head, v_stride_tok,
+                            v_stride_head);
+  if (status != PA_OK) return status;
+  if (q_stride_tok < 0 || q_stride_head < 0 || q_out_stride_tok < 0 || q_out_stride_head < 0 ||
+      max_position <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!q || !q_out || !k || !v || !positions || !cos_table || !sin_table || !slot_mapping)
+    return PA_ERR_INVALID_ARG;
+  pa::RopeArgs a;
+  a.kpool = pool->k;
+  a.vpool = pool->v;
+  a.kscale = pool->k_scale;
+  a.vscale = pool->v_scale;
+  a.num_blocks = pool->num_blocks;
+  a.hkv = pool->kv_heads;
+  a.q = q;
+  a.q_st = q_stride_tok;
+  a.q_sh = q_stride_head;
+  a.q_heads = q_heads;
+  a.q_out = q_out;
+  a.qo_st = q_out_stride_tok;
+  a.qo_sh = q_out_stride_head;
+  a.k = k;
+  a.k_st = k_stride_tok;
+  a.k_sh = k_stride_head;
+  a.v = v;
+  a.v_st = v_stride_tok;
+  a.v_sh = v_stride_head;
+  a.num_tokens = num_tokens;
+  a.positions = positions;
+  a.cos_table = cos_table;
+  a.sin_table = sin_table;
+  a.max_position = max_position;
+  a.slots = slot_mapping;
+  return launched(pa::launch_rope_store(*pool, a, src_dtype, (hipStream_t)stream));
+}
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t split_tokens) {

@@ -55,6 +55,34 @@ struct StepRows {
 int launch_decode_step(const pa_kv_pool_t& pool, const DecodeArgs& a, const StepRows& rows,
                        hipStream_t stream);
 
+// Fused RoPE + store of a step's new tokens (pa_rope_store_kv).
+struct RopeArgs {
+  void* kpool;
+  void* vpool;
+  float* kscale;
+  float* vscale;
+  int64_t num_blocks;
+  int hkv;
+  const void* q;
+  int64_t q_st, q_sh;
+  int q_heads;
+  void* q_out;
+  int64_t qo_st, qo_sh;
+  const void* k;
+  int64_t k_st, k_sh;
+  const void* v;
+  int64_t v_st, v_sh;
+  int64_t num_tokens;
+  const int64_t* positions;
+  const float* cos_table;  // [max_position, head_dim / 2]
+  const float* sin_table;
+  int64_t max_position;
+  const int64_t* slots;
+};
+
+int launch_rope_store(const pa_kv_pool_t& pool, const RopeArgs& a, int src_dtype,
+                      hipStream_t stream);
+
 struct PrefillArgs {
   void* out;
   int64_t out_st, out_sh;

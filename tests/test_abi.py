@@ -30,6 +30,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared()
     assert set(names) >= {"pa_store_kv", "pa_decode", "pa_varlen_prefill", "pa_decode_step",
+                          "pa_rope_store_kv",
                           "pa_decode_workspace_bytes", "pa_status_string",
                           "pa_decode_default_split_tokens", "pa_varlen_prefill_workspace_bytes"}
     for n in names:
@@ -125,6 +126,31 @@ def test_decode_step_validation(lib):
                               ctypes.byref(fp8), 0xC000, 0xD000, pa.PA_FP8_E4M3, 256, 128, 256,
                               128, 0xE000, 0xA000, 8, 0xB000, 128, 0.1, 128, 0, 0,
                               None) == INVALID               # FP8 pools take bf16/f32 rows
+
+
+def rope(lib, pool, src=pa.PA_BF16, T=4, Hq=12, q=0x9000, qo=0x9800, pos=0xF000, cos=0xF800,
+         maxp=64, sm=0xE000, qst=1536):
+    return lib.pa_rope_store_kv(ctypes.byref(pool), q, qst, 128, Hq, qo, 1536, 128, 0xC000,
+                                0xD000, src, T, 256, 128, 256, 128, pos, cos, cos + 0x400,
+                                maxp, sm, None)
+
+
+def test_rope_store_validation(lib):
+    p = fake_pool()
+    assert rope(lib, p, T=0) == OK
+    assert rope(lib, p, T=-1) == INVALID
+    assert rope(lib, p, Hq=13) == INVALID                   # not a multiple of kv_heads
+    assert rope(lib, p, src=pa.PA_F32) == INVALID           # f32 rows into a bf16 pool
+    assert rope(lib, p, q=0) == INVALID
+    assert rope(lib, p, qo=0) == INVALID
+    assert rope(lib, p, pos=0) == INVALID
+    assert rope(lib, p, cos=0) == INVALID
+    assert rope(lib, p, sm=0) == INVALID
+    assert rope(lib, p, maxp=0) == INVALID
+    assert rope(lib, p, qst=-1) == INVALID
+    fp8 = fake_pool(pa.PA_FP8_E4M3, scales=True)
+    assert rope(lib, fp8, src=pa.PA_FP8_E4M3) == INVALID    # sources are bf16 or f32
+    assert rope(lib, fake_pool(head_dim=96)) == UNSUPPORTED
 
 
 def test_default_split_and_workspace_bytes(lib):

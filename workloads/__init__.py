@@ -329,3 +329,13 @@ def fill_device_normal_(tensor, seed):
         flat[a:b] = torch.randn(b - a, generator=g, device=tensor.device,
                                 dtype=torch.float32).to(tensor.dtype)
     return tensor
+
+
+def rope_tables(max_position, head_dim, base=1.0e6):
+    """cos / sin tables, float32 [max_position, head_dim/2], of the usual rotary schedule
+    angle(p, i) = p * base^(-2i/head_dim) (Qwen2.5 uses base 1e6). Any table is a valid
+    input to the fused RoPE store; this one is the realistic case."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv = base ** (-2.0 * i / head_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
