@@ -13,7 +13,9 @@
  *                      softmax; long contexts are split and merged by log-sum-exp;
  *                      pa_decode_step stores the step's new rows and attends in one;
  *   pa_varlen_prefill  a flat batch of query chunks (cu_seqlens) attends, causally, the
- *                      cached prefix plus the chunk itself, per sequence.
+ *                      cached prefix plus the chunk itself, per sequence;
+ *   pa_bm_*            a host block manager (allocation, prefix sharing, copy-on-
+ *                      write) that produces block_tables and slots for the above.
  *
  * Sources (web pages; cited below by tag and section):
  *   [P1] lvyufeng.github.io/PocketLLM .../phase3_3_completion_summary
@@ -29,10 +31,11 @@
  *
  * Conventions shared by all calls
  * --------------------------------
- *  - Every array argument is a DEVICE pointer owned by the caller. The library never
- *    allocates, frees or caches device memory and keeps no global mutable state: all
- *    addressing is passed explicitly on every call, as [P1] "design decisions /
- *    explicit parameter passing" argues against a hidden current slot.
+ *  - Every array argument of a kernel call is a DEVICE pointer owned by the caller. The
+ *    library never allocates, frees or caches device memory and keeps no global
+ *    mutable state: all addressing is passed explicitly on every call, as [P1] "design
+ *    decisions / explicit parameter passing" argues against a hidden current slot (the
+ *    host block manager keeps its state in the handle the caller creates).
  *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
  *    default stream). They return after enqueueing and never synchronise.
  *  - Element strides are in ELEMENTS, not bytes; the innermost (head_dim) stride is
@@ -323,6 +326,73 @@ int pa_varlen_prefill(void *out, int64_t out_stride_tok, int64_t out_stride_head
                       int32_t max_blocks_per_seq, const int32_t *context_lens,
                       int32_t max_context_len, float scale, int32_t split_tokens,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_copy_blocks - copy whole pool blocks: for i < num_pairs, block dst_blocks[i] of K
+ * and of V (and the matching rows of k_scale / v_scale of a quantised pool) becomes a
+ * copy of block src_blocks[i]. src_blocks / dst_blocks are int32 DEVICE arrays; a pair
+ * with an id outside [0, num_blocks) is skipped. Used for the copy-on-write that
+ * pa_bm_append_token reports. The destinations must be distinct and not also sources.
+ */
+int pa_copy_blocks(const pa_kv_pool_t *pool, const int32_t *src_blocks,
+                   const int32_t *dst_blocks, int32_t num_pairs, void *stream);
+
+/*
+ * Block manager (host only; no device memory, no stream): hands out a pool's blocks to
+ * sequences and builds the block_tables / context_lens / slot_mapping the kernels take.
+ *
+ * Defined by [P4] "KV Cache management" (one global pool of fixed-size blocks allocated
+ * up front, blocks allocated and recycled per request, a logical -> physical block_table
+ * per request that lives as long as the request) and the cross-request prefix sharing
+ * [P2] plans after its per-slot prefix caches ("risk 3": RadixAttention-like sharing).
+ * The policy is this library's (the pages fix none of it):
+ *  - a new block is the lowest-numbered free block that holds no cached prefix; only
+ *    when there is none is a cached free block evicted, least recently released first
+ *    (ties: lowest number);
+ *  - with prefix caching on, a block that becomes full is entered in a prefix index
+ *    under a chained hash of (previous block's hash, its block_size token ids), unless
+ *    that hash is already present;
+ *  - pa_bm_add_sequence reuses indexed blocks for the new sequence's leading full blocks
+ *    while they match (hash, parent hash and token ids all equal), never for the block
+ *    of its last token, and reports how many leading tokens are already cached;
+ *  - appending to a shared partial block first moves the sequence to a fresh copy
+ *    (copy-on-write; the caller copies the device rows with pa_copy_blocks);
+ *  - a released sequence returns its blocks last block first.
+ * Every entry point returns PA_OK, PA_ERR_INVALID_ARG (null handle or pointer, unknown
+ * or duplicate sequence id, out-of-range position, table too narrow) or
+ * PA_ERR_WORKSPACE (not enough free blocks; nothing is changed). A handle is not
+ * thread-safe.
+ */
+typedef struct pa_block_manager pa_block_manager_t;
+
+/* num_blocks in [1, 2^31); block_size > 0 (the kernels take 16). NULL on bad input. */
+pa_block_manager_t *pa_bm_create(int64_t num_blocks, int32_t block_size,
+                                 int32_t prefix_caching);
+void pa_bm_destroy(pa_block_manager_t *bm);
+int64_t pa_bm_num_free_blocks(const pa_block_manager_t *bm);
+/* Register a sequence with its num_tokens prompt token ids; *cached_tokens (may be
+ * NULL) receives the number of leading tokens whose blocks were reused. */
+int pa_bm_add_sequence(pa_block_manager_t *bm, int64_t seq_id, const int32_t *token_ids,
+                       int64_t num_tokens, int64_t *cached_tokens);
+/* Extend a sequence by one token: *slot receives its slot; *copy_src / *copy_dst the
+ * block to copy for copy-on-write, or -1 / -1. */
+int pa_bm_append_token(pa_block_manager_t *bm, int64_t seq_id, int32_t token_id,
+                       int64_t *slot, int32_t *copy_src, int32_t *copy_dst);
+/* New sequence child_id sharing all of parent_id's blocks. */
+int pa_bm_fork(pa_block_manager_t *bm, int64_t parent_id, int64_t child_id);
+int pa_bm_free_sequence(pa_block_manager_t *bm, int64_t seq_id);
+/* Token count of a sequence, -1 if unknown. */
+int64_t pa_bm_context_len(const pa_block_manager_t *bm, int64_t seq_id);
+/* Host arrays: block_tables [num_seqs, max_blocks_per_seq] (-1 padded) and, unless NULL,
+ * context_lens [num_seqs], for the given sequences in order. */
+int pa_bm_block_tables(const pa_block_manager_t *bm, const int64_t *seq_ids, int32_t num_seqs,
+                       int32_t max_blocks_per_seq, int32_t *block_tables,
+                       int32_t *context_lens);
+/* Host array slots [count]: the slots of positions first_pos .. first_pos + count - 1. */
+int pa_bm_slots(const pa_block_manager_t *bm, int64_t seq_id, int64_t first_pos,
+                int64_t count, int64_t *slots);
+/* Sequences holding a block (0: free), -1 for a bad handle or id. */
+int32_t pa_bm_block_refcount(const pa_block_manager_t *bm, int32_t block);
 
 #ifdef __cplusplus
 }

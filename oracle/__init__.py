@@ -11,6 +11,8 @@ Modules
          absmax/448 quantiser.
   int8   symmetric int8 codec: absmax/127 per-token-per-head quantiser (nearest
          integer, ties to even, clamp to [-127, 127]) and its dequantisation.
+  blocks reference block manager (allocation, prefix sharing of full blocks, copy-on-
+         write) in plain lists, for the host block manager's index work.
   rope   rotary position embedding (pair i with i + D/2, table-driven, fp32 with every
          operation rounded) and the fused RoPE + KV store built on ref's stores.
   ref    the plain definition: store through slot_mapping, gather the paged KV of each

@@ -14,6 +14,7 @@ is no fallback. PyTorch is used for device memory and streams only.
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +62,18 @@ SIGNATURES = {
     "pa_rope_store_kv": (ctypes.c_int, [ctypes.POINTER(_Pool), _P, _I64, _I64, _I32, _P, _I64,
                                         _I64, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64, _P,
                                         _P, _P, _I32, _P, _P]),
+    "pa_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_Pool), _P, _P, _I32, _P]),
+    "pa_bm_create": (_P, [_I64, _I32, _I32]),
+    "pa_bm_destroy": (None, [_P]),
+    "pa_bm_num_free_blocks": (_I64, [_P]),
+    "pa_bm_add_sequence": (ctypes.c_int, [_P, _I64, _P, _I64, _P]),
+    "pa_bm_append_token": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
+    "pa_bm_fork": (ctypes.c_int, [_P, _I64, _I64]),
+    "pa_bm_free_sequence": (ctypes.c_int, [_P, _I64]),
+    "pa_bm_context_len": (_I64, [_P, _I64]),
+    "pa_bm_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
+    "pa_bm_slots": (ctypes.c_int, [_P, _I64, _I64, _I64, _P]),
+    "pa_bm_block_refcount": (_I32, [_P, _I32]),
     "pa_decode_step": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32,
                                       ctypes.POINTER(_Pool), _P, _P, _I32, _I64, _I64, _I64,
                                       _I64, _P, _P, _I32, _P, _I32, _F, _I32, _P, _SZ, _P]),
@@ -202,6 +215,83 @@ def rope_store_kv(pool, q, k, v, positions, cos_table, sin_table, slot_mapping, 
                                   _stream()),
            "pa_rope_store_kv")
     return q_out
+
+
+def copy_blocks(pool, src_blocks, dst_blocks):
+    """Device copy of pool blocks src_blocks[i] -> dst_blocks[i] (int32 device tensors),
+    K, V and (FP8 / INT8) scales: the copy-on-write of BlockManager.append()."""
+    for t in (src_blocks, dst_blocks):
+        _need(t.dtype == torch.int32 and t.dim() == 1 and t.is_contiguous(),
+              "block lists must be contiguous int32 [n]")
+    _need(src_blocks.shape == dst_blocks.shape, "src/dst lengths differ")
+    _check(lib().pa_copy_blocks(pool.struct, _ptr(src_blocks), _ptr(dst_blocks),
+                                src_blocks.shape[0], _stream()), "pa_copy_blocks")
+
+
+class BlockManager:
+    """Host block manager of one pool (C++ in libpa.so): sequences, their block tables,
+    prefix sharing of full blocks and copy-on-write (policy documented in pa.h)."""
+
+    def __init__(self, num_blocks, block_size=BLOCK_SIZE, prefix_caching=True):
+        self._h = lib().pa_bm_create(num_blocks, block_size, 1 if prefix_caching else 0)
+        if not self._h:
+            raise ValueError("invalid block manager arguments")
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.pa_bm_destroy(h)
+            self._h = None
+
+    @property
+    def num_free(self):
+        return int(lib().pa_bm_num_free_blocks(self._h))
+
+    def add_sequence(self, seq_id, token_ids):
+        """Register a sequence with its prompt; returns the number of leading tokens
+        whose blocks were reused from the prefix cache."""
+        t = np.ascontiguousarray(token_ids, dtype=np.int32)
+        cached = ctypes.c_int64(0)
+        _check(lib().pa_bm_add_sequence(self._h, seq_id, t.ctypes.data_as(ctypes.c_void_p),
+                                        t.size, ctypes.byref(cached)), "pa_bm_add_sequence")
+        return int(cached.value)
+
+    def append(self, seq_id, token_id):
+        """Extend by one token: (slot, copy_src, copy_dst), copy_* = -1 unless the last
+        block had to be copied (copy-on-write)."""
+        slot, cs, cd = ctypes.c_int64(0), ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().pa_bm_append_token(self._h, seq_id, int(token_id), ctypes.byref(slot),
+                                        ctypes.byref(cs), ctypes.byref(cd)), "pa_bm_append_token")
+        return int(slot.value), int(cs.value), int(cd.value)
+
+    def fork(self, parent_id, child_id):
+        _check(lib().pa_bm_fork(self._h, parent_id, child_id), "pa_bm_fork")
+
+    def free(self, seq_id):
+        _check(lib().pa_bm_free_sequence(self._h, seq_id), "pa_bm_free_sequence")
+
+    def context_len(self, seq_id):
+        return int(lib().pa_bm_context_len(self._h, seq_id))
+
+    def block_tables(self, seq_ids, max_blocks_per_seq):
+        """(block_tables int32 [n, max_blocks] -1 padded, context_lens int32 [n])."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        bt = np.empty((ids.size, max_blocks_per_seq), dtype=np.int32)
+        cl = np.empty(ids.size, dtype=np.int32)
+        _check(lib().pa_bm_block_tables(self._h, ids.ctypes.data_as(ctypes.c_void_p), ids.size,
+                                        max_blocks_per_seq, bt.ctypes.data_as(ctypes.c_void_p),
+                                        cl.ctypes.data_as(ctypes.c_void_p)), "pa_bm_block_tables")
+        return bt, cl
+
+    def slots(self, seq_id, first_pos, count):
+        out = np.empty(count, dtype=np.int64)
+        _check(lib().pa_bm_slots(self._h, seq_id, first_pos, count,
+                                 out.ctypes.data_as(ctypes.c_void_p)), "pa_bm_slots")
+        return out
+
+    def refcount(self, block):
+        return int(lib().pa_bm_block_refcount(self._h, block))
 
 
 def decode_workspace_bytes(num_seqs, q_heads, kv_heads, head_dim, max_context_len,

@@ -137,6 +137,17 @@ int pa_rope_store_kv(const pa_kv_pool_t* pool, const void* q, int64_t q_stride_t
   return launched(pa::launch_rope_store(*pool, a, src_dtype, (hipStream_t)stream));
 }
 
+int pa_copy_blocks(const pa_kv_pool_t* pool, const int32_t* src_blocks,
+                   const int32_t* dst_blocks, int32_t num_pairs, void* stream) {
+  int status = PA_OK;
+  if (!pool_shape_ok(pool, &status)) return status;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_blocks || !dst_blocks) return PA_ERR_INVALID_ARG;
+  return launched(pa::launch_copy_blocks(*pool, src_blocks, dst_blocks, num_pairs,
+                                         (hipStream_t)stream));
+}
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t split_tokens) {

@@ -14,6 +14,10 @@ int launch_store(const pa_kv_pool_t& pool, const void* k, const void* v, int src
                  int64_t num_tokens, int64_t k_st, int64_t k_sh, int64_t v_st, int64_t v_sh,
                  const int64_t* slot_mapping, hipStream_t stream);
 
+// Copy K/V blocks (and scales) src[i] -> dst[i], i < n (device arrays).
+int launch_copy_blocks(const pa_kv_pool_t& pool, const int32_t* src, const int32_t* dst, int n,
+                       hipStream_t stream);
+
 struct DecodeArgs {
   void* out;
   int64_t out_st, out_sh;

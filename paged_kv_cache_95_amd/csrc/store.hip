@@ -116,6 +116,37 @@ __global__ void __launch_bounds__(256) store_quant_kernel(
   }
 }
 
+// ---------------------------------------------------------------- whole-block copy
+// Copy-on-write helper: block dst[i] of K and V (and of the scales of a quantised pool)
+// becomes a copy of block src[i]. 16-byte chunks, grid-stride; pairs with an id outside
+// the pool are skipped.
+__global__ void __launch_bounds__(256) copy_blocks_kernel(
+    char* __restrict__ kpool, char* __restrict__ vpool, float* __restrict__ kscale,
+    float* __restrict__ vscale, const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+    int n, int64_t num_blocks, int64_t block_bytes, int scales_per_block) {
+  const int64_t chunks = block_bytes / 16;
+  const int64_t per_pair = 2 * chunks + 2 * scales_per_block;
+  const int64_t total = (int64_t)n * per_pair;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int pair = (int)(i / per_pair);
+    int64_t r = i - (int64_t)pair * per_pair;
+    const int64_t sb = src[pair], db = dst[pair];
+    if (sb < 0 || sb >= num_blocks || db < 0 || db >= num_blocks) continue;
+    if (r < 2 * chunks) {
+      char* pool = r < chunks ? kpool : vpool;
+      const int64_t c = r < chunks ? r : r - chunks;
+      *reinterpret_cast<uint4*>(pool + db * block_bytes + c * 16) =
+          *reinterpret_cast<const uint4*>(pool + sb * block_bytes + c * 16);
+    } else {
+      r -= 2 * chunks;
+      float* sc = r < scales_per_block ? kscale : vscale;
+      const int64_t e = r < scales_per_block ? r : r - scales_per_block;
+      sc[db * scales_per_block + e] = sc[sb * scales_per_block + e];
+    }
+  }
+}
+
 static int grid_for(int64_t work_items, int per_block) {
   int64_t blocks = (work_items + per_block - 1) / per_block;
   const int64_t cap = 256 * 64;  // 64 blocks per CU is plenty for a grid-stride loop
@@ -177,6 +208,19 @@ int launch_store(const pa_kv_pool_t& pool, const void* k, const void* v, int src
           (char*)pool.k, (char*)pool.v, (const char*)k, (const char*)v, k_st, k_sh, v_st, v_sh,
           slot_mapping, num_tokens, hkv, row_bytes, num_slots);
   }
+  return PA_OK;
+}
+
+int launch_copy_blocks(const pa_kv_pool_t& pool, const int32_t* src, const int32_t* dst, int n,
+                       hipStream_t stream) {
+  const int E = pool.dtype == PA_F32 ? 4 : (pool.dtype == PA_BF16 ? 2 : 1);
+  const int64_t block_bytes = (int64_t)pool.block_size * pool.kv_heads * pool.head_dim * E;
+  const bool quant = pool.dtype == PA_FP8_E4M3 || pool.dtype == PA_INT8;
+  const int spb = quant ? pool.block_size * pool.kv_heads : 0;
+  const int grid = grid_for((int64_t)n * (2 * block_bytes / 16 + 2 * spb), 256);
+  copy_blocks_kernel<<<grid, 256, 0, stream>>>((char*)pool.k, (char*)pool.v, pool.k_scale,
+                                               pool.v_scale, src, dst, n, pool.num_blocks,
+                                               block_bytes, spb);
   return PA_OK;
 }
 
