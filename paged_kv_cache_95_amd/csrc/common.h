@@ -160,13 +160,16 @@ constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
 constexpr int kRowRor12 = 0x12C;
 
+// All rows and banks enabled and bound_ctrl set: every control used here (quad perms,
+// row mirrors, row rotates) reads an in-range lane, so no lane keeps an "old" value and
+// the destination needs no initialising move.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

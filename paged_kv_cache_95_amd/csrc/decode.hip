@@ -91,7 +91,7 @@ struct DecodeState {
   using Gm = Geom<KVT, D>;
   float acc[G][Gm::EV];
   float m[G];  // running max of this lane's DPP row (log2 domain)
-  float l[G];  // running sum of this lane's DPP row
+  float l[G];  // running sum over this lane's own K tokens (half of its DPP row's)
 };
 
 template <int KVT, int D, int G, bool MASKED>
@@ -167,9 +167,12 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
 #pragma unroll
       for (int k = 0; k < 2; ++k) p_own[k][h] = fast_exp2(x[k] - m_new);
     }
+    if constexpr (!kQuant<KVT>) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) p_oth[k][h] = dpp<kRowMirror>(p_own[k][h]);
-    st.l[h] = fmaf(st.l[h], alpha, (p_own[0][h] + p_oth[0][h]) + (p_own[1][h] + p_oth[1][h]));
+      for (int k = 0; k < 2; ++k) p_oth[k][h] = dpp<kRowMirror>(p_own[k][h]);
+    }
+    // sum over this lane's own two tokens; the half-row mirror is added once per item
+    st.l[h] = fmaf(st.l[h], alpha, p_own[0][h] + p_own[1][h]);
     st.m[h] = m_new;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
       // alpha is uniform over the DPP row, and the V-lanes of row r own row r's acc
@@ -471,7 +474,8 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
     float M = fmaxf(st.m[h], __shfl_xor(st.m[h], 16));
     M = fmaxf(M, __shfl_xor(M, 32));
     const float f = st.m[h] == NEG_INF ? 0.0f : fast_exp2(st.m[h] - M);
-    float lr = st.l[h] * f;
+    // l counts this lane's own tokens; the mirrored lane of the row holds the other two
+    float lr = (st.l[h] + dpp<kRowMirror>(st.l[h])) * f;
     lr += __shfl_xor(lr, 16);
     lr += __shfl_xor(lr, 32);
 #pragma unroll
