@@ -276,19 +276,22 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PfArgs a) {
     // ---- online softmax; lane holds keys kbase + 32nn + 8(j/4) + 4hl + j%4 of its row
     const bool need_mask = kbase + kPfKeys - 1 > wave_first_limit;
     // raw scores: the (positive) scale is applied once, fused into the exponent
+    if (need_mask) {
+      // only the tiles that reach past the wave's first row (a uniform branch, so the
+      // compares are not paid on the other tiles): key index relative to this lane's
+      // limit, against the accumulator's compile-time key offsets
+      const int lim = my_limit - kbase - 4 * hl;
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (32 * nn + 8 * (j >> 2) + (j & 3) > lim) sacc[nn][j] = NEG_INF;
+    }
     float tmax = NEG_INF;
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float x = sacc[nn][j];
-        if (need_mask) {
-          const int key = kbase + 32 * nn + 8 * (j >> 2) + 4 * hl + (j & 3);
-          x = key <= my_limit ? x : NEG_INF;
-        }
-        sacc[nn][j] = x;
-        tmax = fmaxf(tmax, x);
-      }
+      for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, sacc[nn][j]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float sl2 = a.scale_log2;
     const float m_new = fmaxf(m_run, tmax * sl2);
