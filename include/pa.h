@@ -309,7 +309,11 @@ int pa_decode_step(void *out, int64_t out_stride_tok, int64_t out_stride_head, c
  *                on this value and each sequence's own (n_s, context_lens[s]).
  *   workspace    16-byte aligned device scratch of at least pa_varlen_prefill_workspace_bytes(...)
  *                bytes for the same (total_tokens, q_heads, head_dim, max_context_len,
- *                split_tokens); may be NULL when that is 0; contents on entry ignored.
+ *                split_tokens); contents on entry ignored. It holds the call's work
+ *                list (built on the device from cu_seqlens and context_lens, longest
+ *                items first, claimed by persistent workgroups) and, when a row tile's
+ *                keys exceed split_tokens, the per-chunk partials. Calls that share a
+ *                workspace must be ordered (same stream); overlapping calls race.
  *   Other arguments as in pa_decode. A chunk of length 1 is a decode row.
  * Supported dtypes: (q BF16, pool BF16). QK^T and PV run on the matrix cores with
  * bf16 operands (P rounded to bf16) and fp32 accumulation.

@@ -300,8 +300,12 @@ size_t pa_varlen_prefill_workspace_bytes(int64_t total_tokens, int32_t q_heads,
     return 0;
   const int split = split_tokens == 0 ? pa::kPrefillDefaultSplit : split_tokens;
   const int64_t chunks = ((int64_t)max_context_len + split - 1) / split;
-  if (chunks <= 1) return 0;
-  return (size_t)total_tokens * q_heads * chunks * (head_dim + 1) * sizeof(float);
+  // work list, then (several key chunks) the partials: o [T, Hq, chunks, D], lse
+  const size_t plan = (size_t)(pa::kPfPlanHeaderBytes +
+                               pa::prefill_plan_bound(total_tokens, q_heads, chunks) *
+                                   pa::kPfPlanEntryBytes);
+  if (chunks <= 1) return plan;
+  return plan + (size_t)total_tokens * q_heads * chunks * (head_dim + 1) * sizeof(float);
 }
 
 int pa_varlen_prefill(void* out, int64_t out_stride_tok, int64_t out_stride_head,
@@ -333,12 +337,13 @@ int pa_varlen_prefill(void* out, int64_t out_stride_tok, int64_t out_stride_head
   const int max_chunks = (max_context_len + split - 1) / split;
   const size_t need = pa_varlen_prefill_workspace_bytes(total_tokens, q_heads, pool->head_dim,
                                                         max_context_len, split);
-  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u) != 0))
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u) != 0)
     return PA_ERR_WORKSPACE;
   const int64_t tiles = ((int64_t)max_q_len * (q_heads / pool->kv_heads) + 127) / 128;
-  // prefill grid, and the merge grid (at most 4 workgroups per row tile)
+  const int64_t plan_bound = pa::prefill_plan_bound(total_tokens, q_heads, max_chunks);
+  // work items, the merge grid (at most 4 workgroups per row tile) and the work list
   if (tiles * std::max(max_chunks, 4) * pool->kv_heads * num_seqs >= (int64_t)1 << 31 ||
-      total_tokens * q_heads >= (int64_t)1 << 31)
+      total_tokens * q_heads >= (int64_t)1 << 31 || plan_bound >= (int64_t)1 << 31)
     return PA_ERR_UNSUPPORTED;
 
   pa::PrefillArgs a;
@@ -360,9 +365,13 @@ int pa_varlen_prefill(void* out, int64_t out_stride_tok, int64_t out_stride_head
   a.scale = scale;
   a.split_keys = split;
   a.max_chunks = max_chunks;
-  a.ws_o = (float*)workspace;
-  a.ws_lse = need > 0 ? a.ws_o + (size_t)total_tokens * q_heads * max_chunks * pool->head_dim
-                      : nullptr;
+  a.plan = workspace;
+  a.plan_bound = plan_bound;
+  const size_t plan_bytes = (size_t)(pa::kPfPlanHeaderBytes + plan_bound * pa::kPfPlanEntryBytes);
+  a.ws_o = max_chunks > 1 ? (float*)((char*)workspace + plan_bytes) : nullptr;
+  a.ws_lse = max_chunks > 1
+                 ? a.ws_o + (size_t)total_tokens * q_heads * max_chunks * pool->head_dim
+                 : nullptr;
   return launched(pa::launch_prefill(*pool, a, (hipStream_t)stream));
 }
 

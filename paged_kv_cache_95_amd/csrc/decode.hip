@@ -937,19 +937,6 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   if (t == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Resident workgroups of a kernel on the whole device (CUs x workgroups per CU).
-template <typename K>
-static int64_t resident_workgroups(K kernel) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kWaves, 0) !=
-          hipSuccess ||
-      cus <= 0 || per_cu <= 0)
-    return 1024;
-  return (int64_t)cus * per_cu;
-}
-
 // step != nullptr: a decode step whose new rows are stored first (folded into the
 // single-launch kernel when that schedule runs and the rows allow it, else a store
 // launch ahead of the decode).
@@ -1013,7 +1000,7 @@ static int launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, const 
   const int64_t steps = (items + kWaves - 1) / kWaves;  // upper bound of workgroup steps
   if (a.num_seqs <= kMaxCompactSeqs) {
     auto kern = decode_compact_kernel<KVT, D, G, QT>;
-    const int64_t grid = std::min(steps, resident_workgroups(kern));
+    const int64_t grid = std::min(steps, resident_workgroups(kern, 64 * kWaves));
     kern<<<(unsigned)grid, 64 * kWaves, 0, stream>>>(sa);
   } else {
     decode_split_kernel<KVT, D, G, QT><<<(unsigned)steps, 64 * kWaves, 0, stream>>>(sa);

@@ -10,6 +10,19 @@ namespace pa {
 
 constexpr int kBlockSize = 16;
 
+// Workgroups of `threads` threads of a kernel resident at once on the current device
+// (CUs x workgroups per CU); the grid size of the persistent kernels.
+template <typename K>
+inline int64_t resident_workgroups(K kernel, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0)
+    return 1024;
+  return (int64_t)cus * per_cu;
+}
+
 int launch_store(const pa_kv_pool_t& pool, const void* k, const void* v, int src_dtype,
                  int64_t num_tokens, int64_t k_st, int64_t k_sh, int64_t v_st, int64_t v_sh,
                  const int64_t* slot_mapping, hipStream_t stream);
@@ -103,11 +116,23 @@ struct PrefillArgs {
   float scale;
   int split_keys;  // keys per work item, multiple of 64
   int max_chunks;  // ceil(max_context_len / split_keys)
+  void* plan;      // work list: kPfPlanHeaderBytes of header, then plan_bound entries
+  int64_t plan_bound;
   float* ws_o;     // [total_tokens, q_heads, max_chunks, head_dim] when max_chunks > 1
   float* ws_lse;   // [total_tokens, q_heads, max_chunks]
 };
 
 constexpr int kPrefillDefaultSplit = 1024;
+
+// The prefill workspace starts with its work list: a header (entry count and the
+// claim counter) and one 32-byte entry per (sequence, row tile, key chunk) that has
+// work. Entries are at most one per 128 query rows (plus one per non-empty chunk) per
+// key chunk, bounded without knowing the KV-head count by taking G <= q_heads.
+constexpr int64_t kPfPlanHeaderBytes = 256;
+constexpr int64_t kPfPlanEntryBytes = 32;
+inline int64_t prefill_plan_bound(int64_t total_tokens, int64_t q_heads, int64_t max_chunks) {
+  return ((total_tokens * q_heads + 127) / 128 + total_tokens) * max_chunks;
+}
 
 int launch_prefill(const pa_kv_pool_t& pool, const PrefillArgs& a, hipStream_t stream);
 

@@ -27,6 +27,8 @@
 //    split tiles write (o, lse) partials and a small kernel merges them by
 //    log-sum-exp. The next 64-key tile is fetched into registers while the current
 //    one is multiplied.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -68,12 +70,32 @@ struct PfArgs {
   int q_heads;
   int split_keys;    // keys per work item (multiple of 64)
   int max_chunks;    // ceil(max_context_len / split_keys)
+  char* plan;        // work list (header, then entries)
+  int64_t plan_bound;
   float* ws_o;       // [total_tokens, q_heads, max_chunks, D] partials (max_chunks > 1)
   float* ws_lse;     // [total_tokens, q_heads, max_chunks]
 };
 
+// Work list written by prefill_plan_kernel at the start of the workspace: the number of
+// entries, then the entries, costliest first. An entry is one (sequence, row tile, key
+// chunk) with work; it stands for kv_heads work items (one per KV head).
+struct PfPlanHeader {
+  int32_t entries;
+};
+struct PfEntry {
+  int32_t s, mt, chunk, t_begin;  // sequence, row tile, key chunk, first token
+  int32_t n, L, cost, pad;        // chunk length, clamped context length, 64-key tiles
+};
+static_assert(sizeof(PfEntry) == kPfPlanEntryBytes, "entry size");
+static_assert(sizeof(PfPlanHeader) <= kPfPlanHeaderBytes, "header size");
+
+// One work item: 128 flattened query rows of (sequence, KV head g) against one key chunk.
+// Called by every thread of the workgroup with the same arguments (its barriers are
+// uniform); Ks / Vt are the workgroup's LDS tiles.
 template <int D, int G>
-__global__ void __launch_bounds__(256, 2) prefill_kernel(PfArgs a) {
+__device__ __forceinline__ void prefill_item(const PfArgs& a, uint16_t* __restrict__ Ks,
+                                             uint16_t* __restrict__ Vt, const PfEntry& e,
+                                             int g) {
   const uint16_t* __restrict__ kpool = a.kpool;
   const uint16_t* __restrict__ vpool = a.vpool;
   const int64_t num_blocks = a.num_blocks;
@@ -87,8 +109,6 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PfArgs a) {
   constexpr int DSTEPS = D / 16;              // k-steps of the QK^T MFMA
   constexpr int DT = D / 32;                  // 32-wide d tiles of O^T
   constexpr float NEG_INF = -__builtin_huge_valf();
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kPfKeys * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VROW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -96,31 +116,15 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PfArgs a) {
   const int hl = lane >> 5;     // which half of the wave (k-slot group of the MFMA)
   const int l32 = lane & 31;
 
-  // blockIdx.x -> (row tile, key chunk, kv head, sequence); within a chunk the last
-  // (longest) row tiles come first
-  const int mt = a.tiles_per_seq - 1 - (int)(blockIdx.x % a.tiles_per_seq);
-  const int rest = blockIdx.x / a.tiles_per_seq;
-  const int chunk = rest % a.max_chunks;
-  const int rest2 = rest / a.max_chunks;
-  const int g = rest2 % hkv;
-  const int s = rest2 / hkv;
-  const int t_begin = a.cu_seqlens[s];
-  const int t_end = a.cu_seqlens[s + 1];
-  // chunks outside [0, total_tokens] break the cu_seqlens contract: skip them rather
-  // than read or write outside q / out
-  if (t_begin < 0 || t_end > a.total_tokens) return;
-  const int n = t_end - t_begin;
+  // the plan only lists row tiles with rows and key chunks with keys
+  const int s = e.s, mt = e.mt, chunk = e.chunk, t_begin = e.t_begin, n = e.n, L = e.L;
   const int nrows = n * G;
   const int m0 = mt * kPfRows;
-  if (m0 >= nrows) return;  // whole workgroup: no barrier reached yet
-  // clamp to the host bound (<= max_blocks_per_seq * 16) so table reads stay in the row
-  const int L = min(a.context_lens[s], a.max_context_len);
   const int P = L - n;
   const int m_last = min(m0 + kPfRows, nrows) - 1;
   const int kend = P + m_last / G + 1;  // keys [0, kend) are visible to some row here
   // this work item's key range [k_lo, k_hi)
   const int nchunks = (kend + a.split_keys - 1) / a.split_keys;
-  if (chunk >= nchunks) return;
   const int k_lo = chunk * a.split_keys;
   const int k_hi = min(kend, k_lo + a.split_keys);
 
@@ -372,6 +376,154 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PfArgs a) {
     }
 }
 
+// Persistent prefill: the grid holds at most the resident workgroups; the work items,
+// sorted costliest first, are dealt to them in rounds, alternating direction from round
+// to round (workgroup b takes item b in round 0, item 2*grid - 1 - b in round 1, ...),
+// so that the workgroups with the longest first items get the shortest later ones.
+// The assignment is static (no claim counter: one counter hit by every workgroup at
+// once serialises). Items are independent, so the result does not depend on it.
+template <int D, int G>
+__global__ void __launch_bounds__(256, 2) prefill_kernel(PfArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kPfKeys * (D + kKPad)];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * (kPfKeys + kVPad)];
+  const PfPlanHeader* hdr = reinterpret_cast<const PfPlanHeader*>(a.plan);
+  const PfEntry* entries = reinterpret_cast<const PfEntry*>(a.plan + kPfPlanHeaderBytes);
+  const int64_t items = (int64_t)hdr->entries * a.hkv;
+  const int64_t grid = gridDim.x, b = blockIdx.x;
+  for (int64_t r = 0;; ++r) {
+    const int64_t it = r * grid + ((r & 1) ? grid - 1 - b : b);
+    if (it >= items) break;
+    const int64_t ei = it / a.hkv;
+    const PfEntry e = entries[ei];
+    prefill_item<D, G>(a, Ks, Vt, e, (int)(it - ei * a.hkv));
+  }
+}
+
+// The work list. One workgroup: the sizes of the first kPfPlanSeqCache sequences are
+// loaded once into LDS; every (sequence, row tile) pair contributes its key chunks
+// (all but the last cover split_keys keys), counted into buckets by cost (64-key
+// tiles, capped), then written costliest bucket first, so the persistent workgroups
+// take the longest items first (longest-processing-time-first list scheduling).
+constexpr int kPfPlanThreads = 1024;
+constexpr int kPfPlanBuckets = 64;
+constexpr int kPfPlanSeqCache = 4 * kPfPlanThreads;
+
+__global__ void __launch_bounds__(kPfPlanThreads) prefill_plan_kernel(PfArgs a) {
+  __shared__ int hist[kPfPlanBuckets];
+  __shared__ int cursor[kPfPlanBuckets];
+  __shared__ int c_begin[kPfPlanSeqCache], c_n[kPfPlanSeqCache], c_len[kPfPlanSeqCache];
+  const int tid = threadIdx.x;
+  const int G = a.q_heads / a.hkv;
+  if (tid < kPfPlanBuckets) hist[tid] = 0;
+  const int cached = min(a.num_seqs, kPfPlanSeqCache);
+  {
+    int tb[4], te[4], cl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = tid + kPfPlanThreads * u;
+      if (s < cached) {
+        tb[u] = a.cu_seqlens[s];
+        te[u] = a.cu_seqlens[s + 1];
+        cl[u] = a.context_lens[s];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = tid + kPfPlanThreads * u;
+      if (s < cached) {
+        c_begin[s] = tb[u];
+        c_n[s] = te[u] - tb[u];
+        c_len[s] = min(cl[u], a.max_context_len);
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t pairs = (int64_t)a.num_seqs * a.tiles_per_seq;
+  const int S = a.split_keys;
+  const int cost_full = S / kPfKeys;
+  auto bucket = [](int cost) { return min(cost, kPfPlanBuckets - 1); };
+  // (sequence, row tile) pair p: its entry template and number of chunks (0: no work)
+  auto visit = [&](int64_t p, PfEntry& e, int& nch, int& cost_last) {
+    const int s = (int)(p / a.tiles_per_seq);
+    const int mt = (int)(p - (int64_t)s * a.tiles_per_seq);
+    int tb, n, L;
+    if (s < kPfPlanSeqCache) {
+      tb = c_begin[s];
+      n = c_n[s];
+      L = c_len[s];
+    } else {
+      tb = a.cu_seqlens[s];
+      n = a.cu_seqlens[s + 1] - tb;
+      L = min(a.context_lens[s], a.max_context_len);
+    }
+    nch = 0;
+    cost_last = 0;
+    // chunks outside [0, total_tokens] break the cu_seqlens contract: no work for them
+    if (tb < 0 || n <= 0 || (int64_t)tb + n > a.total_tokens) return;
+    const int nrows = n * G;
+    const int m0 = mt * kPfRows;
+    if (m0 >= nrows) return;
+    const int kend = L - n + (min(m0 + kPfRows, nrows) - 1) / G + 1;
+    if (kend <= 0) return;  // context shorter than the chunk: nothing visible
+    nch = (kend + S - 1) / S;
+    const int k_lo = (nch - 1) * S;
+    cost_last = (kend + kPfKeys - 1) / kPfKeys - k_lo / kPfKeys;
+    e.s = s;
+    e.mt = mt;
+    e.t_begin = tb;
+    e.n = n;
+    e.L = L;
+    e.pad = 0;
+  };
+  for (int64_t p = tid; p < pairs; p += kPfPlanThreads) {
+    PfEntry e;
+    int nch, cost_last;
+    visit(p, e, nch, cost_last);
+    if (nch > 1) atomicAdd(&hist[bucket(cost_full)], nch - 1);
+    if (nch > 0) atomicAdd(&hist[bucket(cost_last)], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the buckets, costliest first, by the first wave (lane l holds
+  // bucket kPfPlanBuckets - 1 - l); the counts sum to less than 2^31
+  static_assert(kPfPlanBuckets == 64, "one bucket per lane");
+  if (tid < 64) {
+    const int b = kPfPlanBuckets - 1 - tid;
+    const int c = hist[b];
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (tid >= d) incl += o;
+    }
+    cursor[b] = incl - c;
+    if (tid == 63)
+      reinterpret_cast<PfPlanHeader*>(a.plan)->entries = (int32_t)min((int64_t)incl, a.plan_bound);
+  }
+  __syncthreads();
+  PfEntry* entries = reinterpret_cast<PfEntry*>(a.plan + kPfPlanHeaderBytes);
+  for (int64_t p = tid; p < pairs; p += kPfPlanThreads) {
+    PfEntry e;
+    int nch, cost_last;
+    visit(p, e, nch, cost_last);
+    if (nch <= 0) continue;
+    if (nch > 1) {
+      const int pos = atomicAdd(&cursor[bucket(cost_full)], nch - 1);
+      e.cost = cost_full;
+      for (int c = 0; c < nch - 1; ++c) {
+        if (pos + c >= a.plan_bound) break;
+        e.chunk = c;
+        entries[pos + c] = e;
+      }
+    }
+    const int pos = atomicAdd(&cursor[bucket(cost_last)], 1);
+    if (pos < a.plan_bound) {
+      e.chunk = nch - 1;
+      e.cost = cost_last;
+      entries[pos] = e;
+    }
+  }
+}
+
 // Merge of the key-chunk partials. The prefill grid's row tiles are cut into parts of
 // 256 / (D/16) rows; one 256-thread workgroup per (part, row tile, KV head, sequence),
 // one thread per (row, 16-float slice of head_dim), slice fastest so neighbouring
@@ -490,9 +642,14 @@ static void launch_prefill_t(const pa_kv_pool_t& pool, const PrefillArgs& pa_, h
   a.q_heads = pa_.q_heads;
   a.split_keys = pa_.split_keys;
   a.max_chunks = pa_.max_chunks;
+  a.plan = (char*)pa_.plan;
+  a.plan_bound = pa_.plan_bound;
   a.ws_o = pa_.ws_o;
   a.ws_lse = pa_.ws_lse;
-  const int64_t grid = (int64_t)a.tiles_per_seq * a.max_chunks * pool.kv_heads * pa_.num_seqs;
+  prefill_plan_kernel<<<1, kPfPlanThreads, 0, stream>>>(a);
+  // persistent: no more workgroups than fit at once, nor than there are work items
+  const int64_t items = (int64_t)a.tiles_per_seq * a.max_chunks * pool.kv_heads * pa_.num_seqs;
+  const int64_t grid = std::min(items, resident_workgroups(prefill_kernel<D, G>, 256));
   prefill_kernel<D, G><<<(unsigned)grid, 256, 0, stream>>>(a);
   if (a.max_chunks > 1)
     prefill_merge_kernel<D><<<(unsigned)((int64_t)(kPfRows / pf_merge_rows<D>()) *

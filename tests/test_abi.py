@@ -189,9 +189,15 @@ def test_prefill_validation(lib):
     assert prefill(lib, fake_pool(pa.PA_F32), q_dtype=pa.PA_F32) == UNSUPPORTED
     assert prefill(lib, p, split=32) == INVALID               # not a multiple of 64
     assert prefill(lib, p, split=64, ws=0) == WORKSPACE       # 128 keys in 2 chunks
+    # work list: 256-byte header + 32-byte entries, at most one per 128 rows (G <= Hq)
+    # plus one per token, per key chunk; then the partials when a tile has 2+ chunks
+    def plan(T, Hq, chunks):
+        return 256 + 32 * ((T * Hq + 127) // 128 + T) * chunks
     need = lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 128, 64)
-    assert need == 10 * 12 * 2 * 129 * 4
+    assert need == plan(10, 12, 2) + 10 * 12 * 2 * 129 * 4
     assert prefill(lib, p, split=64, ws=0xE000, wsb=need - 4) == WORKSPACE
     assert prefill(lib, p, split=64, ws=0xE004, wsb=need) == WORKSPACE  # not 16-B aligned
-    assert lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 1024, 0) == 0
-    assert lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 1025, 0) == 10 * 12 * 2 * 129 * 4
+    assert prefill(lib, p, ws=0) == WORKSPACE                  # the work list is needed too
+    assert lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 1024, 0) == plan(10, 12, 1)
+    assert (lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 1025, 0)
+            == plan(10, 12, 2) + 10 * 12 * 2 * 129 * 4)
