@@ -41,6 +41,7 @@ constexpr int kPfRows = 128;   // flattened rows per workgroup
 constexpr int kPfKeys = 64;    // keys per iteration
 constexpr int kKPad = 8;       // bf16 elements of padding per K row in LDS
 constexpr int kVPad = 8;       // bf16 elements of padding per V^T row in LDS
+constexpr float kPfLazyMax = 8.0f;  // log2 headroom of the lazily updated row max
 
 __device__ __forceinline__ int vt_pos(int k) {
   // swap bits 2 and 3 of the key index (bits 0-1 and >= 4 unchanged)
@@ -88,6 +89,12 @@ struct PfEntry {
 };
 static_assert(sizeof(PfEntry) == kPfPlanEntryBytes, "entry size");
 static_assert(sizeof(PfPlanHeader) <= kPfPlanHeaderBytes, "header size");
+
+// x[i] for i in 0..3 as selects (a run-time index into a register array would put
+// the array in scratch memory).
+__device__ __forceinline__ int pick4(const int (&x)[4], int i) {
+  return i == 0 ? x[0] : (i == 1 ? x[1] : (i == 2 ? x[2] : x[3]));
+}
 
 // One work item: 128 flattened query rows of (sequence, KV head g) against one key chunk.
 // Called by every thread of the workgroup with the same arguments (its barriers are
@@ -183,44 +190,65 @@ __device__ __forceinline__ void prefill_item(const PfArgs& a, uint16_t* __restri
   uint4 vreg[4];
   // The 64 keys of tile kt are pool blocks kt*4 .. kt*4+3 of the sequence: four block
   // ids, the same for every thread, read as uniform (scalar) loads one tile ahead.
-  auto tile_bids = [&](int kt, int (&bids)[4]) {
+  // The 64 keys of tile kt are pool blocks kt*4 .. kt*4+3 of the sequence. Their ids
+  // are read with vector loads (every lane reads the same address) two tiles ahead of
+  // the fetch that uses them, so the table read never stalls a tile, and are moved to
+  // scalar registers when used: the K addresses are then a scalar block base plus a
+  // loop-invariant 32-bit lane offset.
+  auto load_bids = [&](int kt, int (&raw)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kb = kt * 4 + i;
-      const int raw = kb * kBlockSize < L ? bt_row[kb] : -1;
-      bids[i] = (unsigned)raw < (uint64_t)num_blocks ? raw : -1;
+      raw[i] = kb * kBlockSize < L ? bt_row[kb] : -1;
     }
   };
+  auto to_sgpr = [&](const int (&raw)[4], int (&bids)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = __builtin_amdgcn_readfirstlane(raw[i]);
+      bids[i] = (unsigned)r < (uint64_t)num_blocks ? r : -1;
+    }
+  };
+  const int64_t blk_stride = (int64_t)kBlockSize * tok_stride;  // elements per pool block
+  // byte offsets, so that base + offset is a scalar base plus a zero-extended 32-bit
+  // lane offset (the global load's scalar-base addressing)
+  uint32_t koff[KIT];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int w = tid + 256 * it;
+    koff[it] = (uint32_t)(((w / CH) & 15) * tok_stride + g * D + (w % CH) * 8) * 2u;
+  }
+  const uint32_t voff = (uint32_t)(((4 * v_kq) & 15) * tok_stride + g * D + v_ch * 8);
   auto fetch = [&](int kt, const int (&bids)[4]) {
     const int kbase = kt * kPfKeys;
     // a tile fully inside the context with valid block ids (the common case) needs no
     // per-element guards
     const bool full = kbase + kPfKeys <= L && bids[0] >= 0 && bids[1] >= 0 &&
                       bids[2] >= 0 && bids[3] >= 0;
-    const int vbid = bids[v_kq >> 2];
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
-      const int w = tid + 256 * it;
-      const int key = w / CH, ch = w % CH;
-      const int ka = kbase + key;
-      const int bid = bids[key >> 4];
-      const int64_t off = ((int64_t)bid * kBlockSize + (ka & 15)) * tok_stride + (int64_t)g * D + ch * 8;
+      const int key = (tid + 256 * it) / CH;
+      // the block of K item `it` is the same for the whole wave
+      const int blk = __builtin_amdgcn_readfirstlane(key >> 4);
+      const int bid = pick4(bids, blk);
+      const char* base = reinterpret_cast<const char*>(kpool + (int64_t)max(bid, 0) * blk_stride);
       if (full) {
-        kreg[it] = *reinterpret_cast<const uint4*>(kpool + off);
+        kreg[it] = *reinterpret_cast<const uint4*>(base + koff[it]);
       } else {
         kreg[it] = make_uint4(0, 0, 0, 0);
-        if (ka < L && bid >= 0) kreg[it] = *reinterpret_cast<const uint4*>(kpool + off);
+        if (kbase + key < L && bid >= 0) kreg[it] = *reinterpret_cast<const uint4*>(base + koff[it]);
       }
     }
+    const int vbid = pick4(bids, v_kq >> 2);
+    const uint16_t* vbase = vpool + (int64_t)max(vbid, 0) * blk_stride + voff;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int ka = kbase + 4 * v_kq + r;
-      const int64_t off = ((int64_t)vbid * kBlockSize + (ka & 15)) * tok_stride + (int64_t)g * D + v_ch * 8;
       if (full) {
-        vreg[r] = v_has ? *reinterpret_cast<const uint4*>(vpool + off) : make_uint4(0, 0, 0, 0);
+        vreg[r] = v_has ? *reinterpret_cast<const uint4*>(vbase + r * tok_stride) : make_uint4(0, 0, 0, 0);
       } else {
         vreg[r] = make_uint4(0, 0, 0, 0);
-        if (v_has && ka < L && vbid >= 0) vreg[r] = *reinterpret_cast<const uint4*>(vpool + off);
+        if (v_has && ka < L && vbid >= 0) vreg[r] = *reinterpret_cast<const uint4*>(vbase + r * tok_stride);
       }
     }
   };
@@ -251,18 +279,26 @@ __device__ __forceinline__ void prefill_item(const PfArgs& a, uint16_t* __restri
 
   const int kt0 = k_lo / kPfKeys;
   const int ntiles = (k_hi + kPfKeys - 1) / kPfKeys;
-  int bids[4], bids_next[4];
+  const bf2 kOnesBf2 = {(__bf16)1.0f, (__bf16)1.0f};
+  int raw_next[4];  // block ids of tile kt + 1, loaded during tile kt - 1
   if (kt0 < ntiles) {
-    tile_bids(kt0, bids);
-    fetch(kt0, bids);
+    int raw0[4], b0[4];
+    load_bids(kt0, raw0);
+    to_sgpr(raw0, b0);
+    fetch(kt0, b0);
+    if (kt0 + 1 < ntiles) load_bids(kt0 + 1, raw_next);
   }
   for (int kt = kt0; kt < ntiles; ++kt) {
     const int kbase = kt * kPfKeys;
-    if (kt + 1 < ntiles) tile_bids(kt + 1, bids_next);
     __syncthreads();  // every wave is done reading the previous tile
     stash();
     __syncthreads();
-    if (kt + 1 < ntiles) fetch(kt + 1, bids_next);
+    if (kt + 1 < ntiles) {
+      int bn[4];
+      to_sgpr(raw_next, bn);
+      fetch(kt + 1, bn);
+      if (kt + 2 < ntiles) load_bids(kt + 2, raw_next);
+    }
     if (!wave_active || kbase > wave_last_limit) continue;
 
     // ---- S^T = K Q^T for keys kbase + [0, 32) and + [32, 64)
@@ -298,23 +334,32 @@ __device__ __forceinline__ void prefill_item(const PfArgs& a, uint16_t* __restri
       for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, sacc[nn][j]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float sl2 = a.scale_log2;
-    const float m_new = fmaxf(m_run, tmax * sl2);
+    // The reference max m_run (log2 units) moves only when this tile's row max exceeds
+    // it by more than kPfLazyMax: probabilities then stay below 2^kPfLazyMax and the
+    // accumulators are rescaled on few tiles instead of on most (o / l is the same for
+    // any reference). The first tile with a visible key always moves it.
+    const float t2 = tmax * sl2;
+    const float m_new = t2 > m_run + kPfLazyMax ? t2 : m_run;
     // rows past the chunk (my_limit = -1) see no key at all: keep them at zero
     const float m_use = m_new == NEG_INF ? 0.0f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
+    // the row sum is taken over the bf16-rounded probabilities that multiply V, two
+    // per dot2
     float psum = 0.0f;
     bf16x8_t pb[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float pv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = fast_exp2(fmaf(sacc[t >> 1][8 * (t & 1) + i], sl2, -m_use));
-        psum += pv[i];
-      }
+      for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(sacc[t >> 1][8 * (t & 1) + i], sl2, -m_use));
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[t][i] = (__bf16)pv[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf2 pp = {pb[t][2 * i], pb[t][2 * i + 1]};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf2, psum, false);
+      }
     }
     l_run = fmaf(l_run, alpha, psum);
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
