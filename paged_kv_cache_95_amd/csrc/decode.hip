@@ -371,7 +371,9 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
   const int t0 = split * a.split_tokens;
   const int t1 = min(L, t0 + a.split_tokens);
   const int jb0 = t0 / kBlockSize;
-  const int nblk = t1 > t0 ? (t1 - t0 + kBlockSize - 1) / kBlockSize : 0;
+  // wave-uniform (the split and the length are; the compiler cannot see it), so the
+  // block loop below is a scalar loop
+  const int nblk = __builtin_amdgcn_readfirstlane(t1 > t0 ? (t1 - t0 + kBlockSize - 1) / kBlockSize : 0);
   const int bid_lane = in.bid_lane;
   const uint32_t (&qw)[G][Gm::QW] = in.qw;
 
@@ -454,17 +456,24 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
   // ring of NB block buffers: block j + NB - 1 is requested before block j is used
   constexpr int NB = RingDepth<KVT, G>::value;
   BlockBuf<KVT, D> ring[NB];
+  if (nblk > 0) {
+    // every request is unconditional (past the last block, the last block is requested
+    // again: its lines were just read), so the same loads are in flight on every path
+    // and waiting for block j never waits for the blocks requested after it
 #pragma unroll
-  for (int p = 0; p < NB - 1; ++p)
-    if (p < nblk) load(ring[p], p);
-  for (int j0 = 0; j0 < nblk; j0 += NB) {
+    for (int p = 0; p < NB - 1; ++p) load(ring[p], min(p, nblk - 1));
+    int j0 = 0;
+    for (; j0 + NB <= nblk; j0 += NB) {
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int j = j0 + u;
-      if (j >= nblk) break;
-      if (j + NB - 1 < nblk) load(ring[(u + NB - 1) % NB], j + NB - 1);
-      process(ring[u]);
+      for (int u = 0; u < NB; ++u) {
+        load(ring[(u + NB - 1) % NB], min(j0 + u + NB - 1, nblk - 1));
+        process(ring[u]);
+      }
     }
+    // fewer than NB blocks left: all of them requested already
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u)
+      if (j0 + u < nblk) process(ring[u]);
   }
 
   // ---- combine the four DPP rows: per head, rescale to the wave max and sum
