@@ -172,6 +172,29 @@ __device__ __forceinline__ int dpp_i(int x) {
   return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
 }
 
+// Exchange with lane ^ 32 / lane ^ 16 through gfx950's lane-swap instructions (VALU, no
+// LDS round trip). With x as both operands, v_permlane32_swap returns (x[l mod 32] in
+// the low half of the first result mirrored up, x of the upper half in the second), so
+// the two results of every lane are {x[l], x[l ^ 32]} in some order; likewise for
+// v_permlane16_swap and rows of 16 lanes. Sums and maxima of the pair are therefore
+// the same on both lanes of a pair (IEEE add and max are commutative).
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -480,20 +480,12 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
   float inv_l[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float M = fmaxf(st.m[h], __shfl_xor(st.m[h], 16));
-    M = fmaxf(M, __shfl_xor(M, 32));
+    const float M = xor32_max(xor16_max(st.m[h]));
     const float f = st.m[h] == NEG_INF ? 0.0f : fast_exp2(st.m[h] - M);
     // l counts this lane's own tokens; the mirrored lane of the row holds the other two
-    float lr = (st.l[h] + dpp<kRowMirror>(st.l[h])) * f;
-    lr += __shfl_xor(lr, 16);
-    lr += __shfl_xor(lr, 32);
+    const float lr = xor32_sum(xor16_sum((st.l[h] + dpp<kRowMirror>(st.l[h])) * f));
 #pragma unroll
-    for (int e = 0; e < Gm::EV; ++e) {
-      float a = st.acc[h][e] * f;
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      st.acc[h][e] = a;
-    }
+    for (int e = 0; e < Gm::EV; ++e) st.acc[h][e] = xor32_sum(xor16_sum(st.acc[h][e] * f));
     inv_l[h] = 1.0f / lr;
     lse2[h] = M + __log2f(lr);
 #pragma unroll

@@ -332,7 +332,7 @@ __device__ __forceinline__ void prefill_item(const PfArgs& a, uint16_t* __restri
     for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
       for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, sacc[nn][j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = xor32_max(tmax);
     const float sl2 = a.scale_log2;
     // The reference max m_run (log2 units) moves only when this tile's row max exceeds
     // it by more than kPfLazyMax: probabilities then stay below 2^kPfLazyMax and the
@@ -378,8 +378,8 @@ __device__ __forceinline__ void prefill_item(const PfArgs& a, uint16_t* __restri
       }
   }
 
+  const float l_tot = xor32_sum(l_run);
   if (!row_ok) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (nchunks > 1) {
     // partial over this key chunk: normalised o and log2-sum-exp; a row that saw no
     // key here (all past its causal limit) gets lse = -inf and weighs nothing
