@@ -493,18 +493,339 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
   }
 }
 
+// ---------------------------------------------------------------- matrix-core item
+// The same item (one KV head, G query heads, one split) for bf16 / FP8 / INT8 pools,
+// with the two products of each 16-token block on the matrix cores: S = K Q^T on
+// v_mfma_f32_16x16x32_bf16 (M = the block's 16 tokens, N = the G heads padded to 16,
+// contraction over head_dim) and O += P V on v_mfma_f32_16x16x16_bf16 (M = heads,
+// contraction over the 16 tokens, N = 16 head-dim slots per step). Only G of the 16
+// head columns are used; the matrix cores are not the bound, the vector ALU was, and
+// the per-block vector work drops to the code conversions and a 4-score softmax.
+//
+// Lane l (n = l % 16, kg = l / 16):
+//  * K operand at step st: token n of the block, eight head dims starting at
+//    mma_kdim<E>(st, kg); the Q operand holds the same dims of head n (zero for
+//    n >= G). The order is chosen so that each K load instruction of a wave covers 64
+//    contiguous bytes of every token row it touches.
+//  * S (accumulator): tokens 4kg + i (i < 4) of head n. The softmax statistics of head
+//    n are shared by the four lanes n + 16kg (lane-swap reductions).
+//  * P operand: the same (head n, tokens 4kg + i): straight from S.
+//  * V operand at step t: tokens 4kg + i, head dim (D/16)*n + t; a lane reads the
+//    D/16 contiguous dims of its four tokens and builds one bf16 quad per step.
+//  * O (accumulator) at step t: heads 4kg + i, dim (D/16)*n + t.
+// The result goes through LDS (`stage`, this wave's [G][D] floats) into the layout of
+// item_partial's output (lane c < 16: dims c*D/16 .. of every head), so the merges
+// downstream are shared. Probabilities enter the PV product as bf16: for bf16 pools as a
+// hi + lo pair (two products, P exact to ~2^-17, like the fp32 P of item_partial); for
+// quantised pools once rounded, with the V scale folded in (as item_partial does).
+template <int KVT>
+struct MmaPath {
+  static constexpr bool value = KVT == kBF16 || kQuant<KVT>;
+};
+constexpr float kMmaLazyMax = 8.0f;  // log2 headroom of the lazily moved reference max
+// blocks in flight per wave: as many as fit in 256 registers with the wave count the
+// kernels run at (a bf16 block buffer is twice a quantised one); the persistent kernel
+// fits three for every dtype
+template <int KVT>
+struct MmaRing {
+  static constexpr int value = kQuant<KVT> ? 3 : 2;
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// First of the eight head dims that lane group kg holds at QK step st (pools of E-byte
+// elements): bf16 rows are read in 16-byte chunks 4*st + kg, 1-byte rows in 16-byte
+// chunks 4*(st/2) + kg of which each step takes one half.
+template <int E>
+__device__ __forceinline__ int mma_kdim(int st, int kg) {
+  return E == 2 ? 32 * st + 8 * kg : 64 * (st >> 1) + 16 * kg + 8 * (st & 1);
+}
+
+template <int D>
+struct MmaIn {
+  uint4 qb[D / 32];  // Q operand (bf16x8) of each QK step
+  int bid_lane;      // block id of block `lane` of the split
+};
+
+template <int E, int D, int G>
+__device__ __forceinline__ void load_mma_inputs(const SplitArgs& a, int s, int split, int g,
+                                                int lane, MmaIn<D>& in) {
+  const int jb0 = split * (a.split_tokens / kBlockSize);
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  in.bid_lane = (lane < a.split_tokens / kBlockSize && jb0 + lane < a.max_blocks_per_seq)
+                    ? bt_row[jb0 + lane]
+                    : 0;
+  const int n = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st) in.qb[st] = make_uint4(0, 0, 0, 0);
+  if (n < G) {
+    const uint16_t* qp = (const uint16_t*)a.q + (int64_t)s * a.q_st +
+                         (int64_t)(g * G + n) * a.q_sh;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+      const int d0 = mma_kdim<E>(st, kg);
+      if (a.q_aligned) {
+        in.qb[st] = *reinterpret_cast<const uint4*>(qp + d0);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)qp[d0 + 2 * e] | ((uint32_t)qp[d0 + 2 * e + 1] << 16);
+        in.qb[st] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+}
+
+template <int KVT, int D>
+struct MmaBuf {
+  static constexpr int E = ElemBytes<KVT>::value;
+  static constexpr int KW = D / 4 * E / 4;     // dwords of K per lane (token n, D/4 dims)
+  static constexpr int VW = D / 16 * E / 4;    // dwords of V per lane per token (D/16 dims)
+  uint32_t k[KW];
+  uint32_t v[4][VW > 0 ? VW : 1];
+  float ks[4], vs[4];  // scales of tokens 4kg + i (quantised pools)
+  int nvalid;
+};
+
+// x[t] of a packed array of 16-bit values (t compile-time)
+template <int N>
+__device__ __forceinline__ uint32_t half_of(const uint32_t (&w)[N], int t) {
+  return (t & 1) ? (w[t >> 1] >> 16) : (w[t >> 1] & 0xFFFFu);
+}
+
+template <int KVT, int D, int G, int NB = MmaRing<KVT>::value>
+__device__ __forceinline__ void item_partial_mma(const SplitArgs& a, const MmaIn<D>& in,
+                                                 int split, int g, int L, int lane,
+                                                 float (&o)[G][D / 16], float (&lse2)[G],
+                                                 float (&sw)[G][D],
+                                                 const char* krow_new = nullptr,
+                                                 const char* vrow_new = nullptr) {
+  using Bf = MmaBuf<KVT, D>;
+  constexpr int E = Bf::E;
+  constexpr int ROW = D * E;
+  constexpr int QS = D / 32;  // QK steps
+  constexpr int PS = D / 16;  // PV steps (head-dim slots per lane)
+  constexpr int KB = D / 4 * E;  // K bytes per lane per token
+  constexpr int VBY = D / 16 * E;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+  static_assert(G <= 8, "two lane groups of O rows");
+  // the split and the length are the same for the whole wave
+  L = __builtin_amdgcn_readfirstlane(L);
+  split = __builtin_amdgcn_readfirstlane(split);
+  const int t0 = split * a.split_tokens;
+  const int t1 = min(L, t0 + a.split_tokens);
+  const int jb0 = t0 / kBlockSize;
+  const int nblk = t1 > t0 ? (t1 - t0 + kBlockSize - 1) / kBlockSize : 0;
+  const int n = lane & 15, kg = lane >> 4;
+  const int64_t blk_bytes = (int64_t)kBlockSize * a.hkv * ROW;
+  const uint32_t koff = (uint32_t)((n * a.hkv + g) * ROW + kg * 16);
+  uint32_t voff[4], sofs[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    voff[r] = (uint32_t)(((4 * kg + r) * a.hkv + g) * ROW + n * VBY);
+    sofs[r] = (uint32_t)((4 * kg + r) * a.hkv + g);
+  }
+
+  auto load = [&](Bf& b, int j) {
+    const int bid_raw = __builtin_amdgcn_readlane(in.bid_lane, j);
+    const bool ok = (unsigned)bid_raw < (uint64_t)a.num_blocks;
+    const int64_t bid = ok ? bid_raw : 0;
+    const int first = (jb0 + j) * kBlockSize;
+    b.nvalid = ok ? min(kBlockSize, L - first) : 0;
+    // the step's new token (context position L - 1) is read from the input row
+    const int pnew = krow_new != nullptr ? L - 1 - first : -1;
+    // 16-byte chunks kg, kg + 4, ... of the row (see mma_kdim)
+    const char* kp = n == pnew ? krow_new + kg * 16 : a.kpool + bid * blk_bytes + koff;
+#pragma unroll
+    for (int c = 0; c < Bf::KW / 4; ++c) {
+      const uint4 x = ld_stream16(kp + 64 * c);
+      b.k[4 * c] = x.x; b.k[4 * c + 1] = x.y; b.k[4 * c + 2] = x.z; b.k[4 * c + 3] = x.w;
+    }
+    const char* vb = a.vpool + bid * blk_bytes;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      load_dwords<Bf::VW>(4 * kg + r == pnew ? vrow_new + n * VBY : vb + voff[r], b.v[r]);
+    if constexpr (kQuant<KVT>) {
+      const int64_t sb = bid * kBlockSize * a.hkv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        b.ks[r] = a.kscale[sb + sofs[r]];
+        b.vs[r] = a.vscale[sb + sofs[r]];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b.ks[r] = b.vs[r] = 1.0f;
+    }
+  };
+
+  f32x4_t oacc[PS];
+#pragma unroll
+  for (int t = 0; t < PS; ++t) oacc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = NEG_INF, l_run = 0.0f;  // of head n, over this lane's tokens (l)
+
+  auto process = [&](const Bf& b) {
+    // ---- S = K Q^T: lane gets tokens 4kg + i of head n
+    f32x4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int st = 0; st < QS; ++st) {
+      uint4 kk;
+      if constexpr (KVT == kBF16) {
+        kk = make_uint4(b.k[4 * st], b.k[4 * st + 1], b.k[4 * st + 2], b.k[4 * st + 3]);
+      } else {
+        const int w0 = 4 * (st >> 1) + 2 * (st & 1);
+        kk = make_uint4(q8x2_to_bf16x2<KVT>(b.k[w0], false), q8x2_to_bf16x2<KVT>(b.k[w0], true),
+                        q8x2_to_bf16x2<KVT>(b.k[w0 + 1], false),
+                        q8x2_to_bf16x2<KVT>(b.k[w0 + 1], true));
+      }
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kk),
+                                                     __builtin_bit_cast(bf16x8_t, in.qb[st]),
+                                                     sacc, 0, 0, 0);
+    }
+    // ---- online softmax of head n (log2 units, scale folded in)
+    float x[4];
+    bool valid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      valid[i] = 4 * kg + i < b.nvalid;
+      const float y = sacc[i] * (a.scale_log2 * b.ks[i]);
+      x[i] = valid[i] ? y : NEG_INF;
+    }
+    const float mb = xor32_max(xor16_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))));
+    // reference max moved only past 2^kMmaLazyMax of headroom (o / l is the same for
+    // any reference); a head that saw no valid token keeps m = -inf and zeros
+    const float m_new = mb > m_run + kMmaLazyMax ? mb : m_run;
+    const float m_use = m_new == NEG_INF ? 0.0f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = valid[i] ? fast_exp2(x[i] - m_use) : 0.0f;
+    l_run = fmaf(l_run, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+      // O rows are heads 4kg + i: their factors come from lanes 4kg + i (n = head)
+      float ah[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) ah[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = kg == 0 ? ah[i] : ah[4 + i];
+#pragma unroll
+        for (int t = 0; t < PS; ++t) oacc[t][i] *= f;
+      }
+    }
+    // P operand (V scales folded in for quantised pools; an invalid token's scale may be
+    // anything, so its probability stays an exact 0 rather than 0 * scale)
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = kQuant<KVT> ? (valid[i] ? p[i] * b.vs[i] : 0.0f) : p[i];
+    const bf2 p01 = bf16x2_rne(pv[0], pv[1]);
+    const bf2 p23 = bf16x2_rne(pv[2], pv[3]);
+    const s16x4_t pa = __builtin_bit_cast(s16x4_t, make_uint2(__builtin_bit_cast(uint32_t, p01),
+                                                              __builtin_bit_cast(uint32_t, p23)));
+    s16x4_t pl;  // bf16 pools: the rounding residue of P, exact to ~2^-17 together
+    if constexpr (KVT == kBF16) {
+      const bf2 r01 = bf16x2_rne(pv[0] - (float)p01[0], pv[1] - (float)p01[1]);
+      const bf2 r23 = bf16x2_rne(pv[2] - (float)p23[0], pv[3] - (float)p23[1]);
+      pl = __builtin_bit_cast(s16x4_t, make_uint2(__builtin_bit_cast(uint32_t, r01),
+                                                  __builtin_bit_cast(uint32_t, r23)));
+    }
+    // ---- O += P V: tokens of invalid rows are exact zeros (garbage could be NaN)
+    uint32_t vw[4][D / 32];  // bf16 pairs of this lane's D/16 dims, per token
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (KVT == kBF16) {
+#pragma unroll
+        for (int w = 0; w < Bf::VW; ++w) vw[r][w] = valid[r] ? b.v[r][w] : 0u;
+      } else {
+        // codes -> bf16 pairs (exact)
+#pragma unroll
+        for (int w = 0; w < Bf::VW; ++w) {
+          const uint32_t c = valid[r] ? b.v[r][w] : 0u;
+          vw[r][2 * w] = q8x2_to_bf16x2<KVT>(c, false);
+          vw[r][2 * w + 1] = q8x2_to_bf16x2<KVT>(c, true);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < PS; ++t) {
+      // bf16 quad (tokens 4kg .. 4kg+3) of head dim slot t
+      const uint32_t lo = half_of(vw[0], t) | (half_of(vw[1], t) << 16);
+      const uint32_t hi = half_of(vw[2], t) | (half_of(vw[3], t) << 16);
+      const s16x4_t vb4 = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb4, oacc[t], 0, 0, 0);
+      if constexpr (KVT == kBF16)
+        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb4, oacc[t], 0, 0, 0);
+    }
+  };
+
+  // ring of NB block buffers, requests unconditional (see item_partial)
+  Bf ring[NB];
+  if (nblk > 0) {
+#pragma unroll
+    for (int p = 0; p < NB - 1; ++p) load(ring[p], min(p, nblk - 1));
+    int j0 = 0;
+    for (; j0 + NB <= nblk; j0 += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        load(ring[(u + NB - 1) % NB], min(j0 + u + NB - 1, nblk - 1));
+        process(ring[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u)
+      if (j0 + u < nblk) process(ring[u]);
+  }
+
+  // ---- per head n: totals over the four lane groups, then O rows normalised
+  const float l_tot = xor32_sum(xor16_sum(l_run));
+  const float lse = l_tot > 0.0f ? m_run + __log2f(l_tot) : NEG_INF;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * kg + i;
+    const float f0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv), i));
+    const float f1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv), 4 + i));
+    const float f = kg == 0 ? f0 : f1;
+    if (h < G) {
+#pragma unroll
+      for (int t = 0; t < PS; ++t) sw[h][PS * n + t] = oacc[t][i] * f;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    lse2[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lse), h));
+    if (lane < 16) {
+#pragma unroll
+      for (int e = 0; e < PS; ++e) o[h][e] = sw[h][PS * lane + e];
+    }
+  }
+}
+
 // Result of one item in the split-then-merge schedule: the final output row when the
 // sequence has a single split, else the partial in the workspace.
-template <int KVT, int D, int G, int QT>
+template <int KVT, int D, int G, int QT, int NBM = MmaRing<KVT>::value>
 __device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split, int g,
                                             int lane) {
   using Gm = Geom<KVT, D>;
-  ItemIn<KVT, D, G> in;
-  load_item_inputs<KVT, D, G, QT>(a, s, split, g, lane, in);
-  const int L = clamped_len(a, s);
-  const int nsplit = num_splits(L, a.split_tokens);
   float o[G][Gm::EV], lse2[G];
-  item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2);
+  int nsplit;
+  if constexpr (MmaPath<KVT>::value) {
+    __shared__ float stage[kWaves][G][D];
+    MmaIn<D> in;
+    load_mma_inputs<ElemBytes<KVT>::value, D, G>(a, s, split, g, lane, in);
+    const int L = clamped_len(a, s);
+    nsplit = num_splits(L, a.split_tokens);
+    item_partial_mma<KVT, D, G, NBM>(a, in, split, g, L, lane, o, lse2, stage[threadIdx.x >> 6]);
+  } else {
+    ItemIn<KVT, D, G> in;
+    load_item_inputs<KVT, D, G, QT>(a, s, split, g, lane, in);
+    const int L = clamped_len(a, s);
+    nsplit = num_splits(L, a.split_tokens);
+    item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2);
+  }
   if (lane >= 16) return;
   const int cv = lane;
   const int d0 = cv * Gm::EV;
@@ -606,7 +927,8 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* wave_sums, int& 
 }
 
 template <int KVT, int D, int G, int QT>
-__global__ void __launch_bounds__(64 * kWaves) decode_compact_kernel(SplitArgs a) {
+__global__ void __launch_bounds__(64 * kWaves, MmaPath<KVT>::value ? 2 : 1)
+    decode_compact_kernel(SplitArgs a) {
   __shared__ int cum[kMaxCompactSeqs + 1];  // cum[s] = splits of sequences before s
   __shared__ int wave_sums[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -635,7 +957,7 @@ __global__ void __launch_bounds__(64 * kWaves) decode_compact_kernel(SplitArgs a
       const int mid = (lo + hi + 1) >> 1;
       if (cum[mid] <= pair) lo = mid; else hi = mid - 1;
     }
-    decode_item<KVT, D, G, QT>(a, lo, pair - cum[lo], g, lane);
+    decode_item<KVT, D, G, QT, 3>(a, lo, pair - cum[lo], g, lane);
   };
   if (a.counters == nullptr) {
     // no workspace (every context fits one split): the b-th contiguous share of steps
@@ -855,8 +1177,12 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   const int c = rest % a.max_chunks;
   const int s = rest / a.max_chunks;
   const int split = c * NW + wave;
+  // the item's inputs are requested before its context length is known
   ItemIn<KVT, D, G> in;
-  load_item_inputs<KVT, D, G, QT>(a, s, split, g, lane, in);
+  MmaIn<D> min_;
+  if constexpr (MmaPath<KVT>::value)
+    load_mma_inputs<ElemBytes<KVT>::value, D, G>(a, s, split, g, lane, min_);
+  else load_item_inputs<KVT, D, G, QT>(a, s, split, g, lane, in);
   const char* krow_new = nullptr;
   const char* vrow_new = nullptr;
   if (a.knew != nullptr) {
@@ -880,7 +1206,11 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   const int ngroups = (nsplit + NW - 1) / NW;
   if (c >= ngroups) return;  // uniform over the workgroup, before any barrier
   float o[G][Gm::EV], lse2[G];
-  item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2, krow_new, vrow_new);
+  if constexpr (MmaPath<KVT>::value)
+    item_partial_mma<KVT, D, G>(a, min_, split, g, L, lane, o, lse2, part_o[wave], krow_new,
+                                vrow_new);
+  else
+    item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2, krow_new, vrow_new);
   if (lane < 16) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
