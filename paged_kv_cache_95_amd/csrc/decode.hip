@@ -590,12 +590,6 @@ struct MmaBuf {
   int nvalid;
 };
 
-// x[t] of a packed array of 16-bit values (t compile-time)
-template <int N>
-__device__ __forceinline__ uint32_t half_of(const uint32_t (&w)[N], int t) {
-  return (t & 1) ? (w[t >> 1] >> 16) : (w[t >> 1] & 0xFFFFu);
-}
-
 template <int KVT, int D, int G, int NB = MmaRing<KVT>::value>
 __device__ __forceinline__ void item_partial_mma(const SplitArgs& a, const MmaIn<D>& in,
                                                  int split, int g, int L, int lane,
@@ -635,25 +629,31 @@ __device__ __forceinline__ void item_partial_mma(const SplitArgs& a, const MmaIn
     const int64_t bid = ok ? bid_raw : 0;
     const int first = (jb0 + j) * kBlockSize;
     b.nvalid = ok ? min(kBlockSize, L - first) : 0;
-    // the step's new token (context position L - 1) is read from the input row
-    const int pnew = krow_new != nullptr ? L - 1 - first : -1;
+    // block bases are wave-uniform (scalar registers); lane offsets are 32-bit, so the
+    // loads use scalar-base addressing
+    const char* kb = a.kpool + bid * blk_bytes;
+    const char* vb = a.vpool + bid * blk_bytes;
+    // the step's new token (context position L - 1) is read from the input row (only
+    // the bf16 single-launch step folds the store in)
+    const int pnew = !kQuant<KVT> && krow_new != nullptr ? L - 1 - first : -1;
     // 16-byte chunks kg, kg + 4, ... of the row (see mma_kdim)
-    const char* kp = n == pnew ? krow_new + kg * 16 : a.kpool + bid * blk_bytes + koff;
+    const char* kp = !kQuant<KVT> && n == pnew ? krow_new + kg * 16 : kb + koff;
 #pragma unroll
     for (int c = 0; c < Bf::KW / 4; ++c) {
       const uint4 x = ld_stream16(kp + 64 * c);
       b.k[4 * c] = x.x; b.k[4 * c + 1] = x.y; b.k[4 * c + 2] = x.z; b.k[4 * c + 3] = x.w;
     }
-    const char* vb = a.vpool + bid * blk_bytes;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      load_dwords<Bf::VW>(4 * kg + r == pnew ? vrow_new + n * VBY : vb + voff[r], b.v[r]);
+      load_dwords<Bf::VW>(!kQuant<KVT> && 4 * kg + r == pnew ? vrow_new + n * VBY : vb + voff[r],
+                          b.v[r]);
     if constexpr (kQuant<KVT>) {
-      const int64_t sb = bid * kBlockSize * a.hkv;
+      const char* ksb = reinterpret_cast<const char*>(a.kscale + bid * kBlockSize * a.hkv);
+      const char* vsb = reinterpret_cast<const char*>(a.vscale + bid * kBlockSize * a.hkv);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        b.ks[r] = a.kscale[sb + sofs[r]];
-        b.vs[r] = a.vscale[sb + sofs[r]];
+        b.ks[r] = *reinterpret_cast<const float*>(ksb + 4 * sofs[r]);
+        b.vs[r] = *reinterpret_cast<const float*>(vsb + 4 * sofs[r]);
       }
     } else {
 #pragma unroll
@@ -751,9 +751,10 @@ __device__ __forceinline__ void item_partial_mma(const SplitArgs& a, const MmaIn
     }
 #pragma unroll
     for (int t = 0; t < PS; ++t) {
-      // bf16 quad (tokens 4kg .. 4kg+3) of head dim slot t
-      const uint32_t lo = half_of(vw[0], t) | (half_of(vw[1], t) << 16);
-      const uint32_t hi = half_of(vw[2], t) | (half_of(vw[3], t) << 16);
+      // bf16 quad (tokens 4kg .. 4kg+3) of head dim slot t: one byte permute per pair
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t lo = __builtin_amdgcn_perm(vw[1][t >> 1], vw[0][t >> 1], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(vw[3][t >> 1], vw[2][t >> 1], sel);
       const s16x4_t vb4 = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
       oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb4, oacc[t], 0, 0, 0);
       if constexpr (KVT == kBF16)
@@ -763,6 +764,7 @@ __device__ __forceinline__ void item_partial_mma(const SplitArgs& a, const MmaIn
 
   // ring of NB block buffers, requests unconditional (see item_partial)
   Bf ring[NB];
+
   if (nblk > 0) {
 #pragma unroll
     for (int p = 0; p < NB - 1; ++p) load(ring[p], min(p, nblk - 1));
