@@ -11,7 +11,10 @@
 // Work item = (sequence s, split i, KV head g) = one wavefront, which serves all G
 // query heads of the group, so every K/V byte is read once; the KV heads of one split
 // are neighbouring work items, so a pool block (all KV heads of 16 tokens) is fetched
-// by one workgroup at about the same time. Lane = 16r + 8h + t (DPP row r, half h):
+// by one workgroup at about the same time. Two item bodies exist: the dot-product one
+// described here (fp32 pools, and bf16 pools with G <= 4) and the matrix-core one
+// further down (bf16 pools with G > 4, FP8, INT8).
+// Dot-product item, lane = 16r + 8h + t (DPP row r, half h):
 //
 //   K side  the 8 lanes of a half-row share one token and each loads 16-byte chunks
 //           t, t+8, ... of its row, so one load instruction covers whole 128-byte lines
@@ -47,7 +50,7 @@ struct Geom {
   static constexpr int NCH = ROW / 16;                // 16-byte chunks per row
   static constexpr int KC = NCH >= 8 ? NCH / 8 : 1;   // chunks per K-lane per token
   static constexpr int EPC = 16 / E;                  // elements per chunk
-  static constexpr int QW = KVT == kF32 ? 4 * KC : (KVT == kBF16 ? 4 * KC : 8 * KC);
+  static constexpr int QW = 4 * KC;                  // query dwords per K-lane per head
   static constexpr int EV = D / 16;                   // elements per V-lane per token
   static constexpr int VB = EV * E;                   // bytes per V-lane per token
   static constexpr int VW = VB / 4;                   // dwords per V-lane per token
@@ -75,15 +78,14 @@ struct BlockBuf {
   using Gm = Geom<KVT, D>;
   uint32_t k[2][Gm::KC * 4];  // [token set][dwords]
   uint32_t v[4][Gm::VW];      // [row token][dwords]
-  float ks[2], vs[2];         // FP8 scales of the K-lane tokens
   int nvalid;
 };
 
 // Blocks kept in flight per wave: as many as the registers allow without losing a
-// wave per SIMD (an FP8 block buffer is half the size of a bf16 one).
-template <int KVT, int G>
+// wave per SIMD.
+template <int G>
 struct RingDepth {
-  static constexpr int value = kQuant<KVT> ? (G <= 4 ? 4 : (G <= 6 ? 3 : 2)) : (G <= 4 ? 3 : 2);
+  static constexpr int value = G <= 4 ? 3 : 2;
 };
 
 template <int KVT, int D, int G>
@@ -116,19 +118,6 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
           s[k][h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][w]),
                                                     __builtin_bit_cast(bf2, b.k[k][w]), s[k][h],
                                                     false);
-    } else if constexpr (kQuant<KVT>) {
-#pragma unroll
-      for (int w = 0; w < Gm::KC * 4; ++w) {
-        const uint32_t p0 = q8x2_to_bf16x2<KVT>(b.k[k][w], false);
-        const uint32_t p1 = q8x2_to_bf16x2<KVT>(b.k[k][w], true);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          s[k][h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][2 * w]),
-                                                    __builtin_bit_cast(bf2, p0), s[k][h], false);
-          s[k][h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[h][2 * w + 1]),
-                                                    __builtin_bit_cast(bf2, p1), s[k][h], false);
-        }
-      }
     } else {
 #pragma unroll
       for (int w = 0; w < Gm::KC * 4; ++w)
@@ -150,7 +139,7 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
       y += dpp<kQuadXor1>(y);
       y += dpp<kQuadXor2>(y);
       y += dpp<kHalfMirror>(y);
-      y *= kQuant<KVT> ? scale_log2 * b.ks[k] : scale_log2;
+      y *= scale_log2;
       x[k] = MASKED ? (valid_k[k] ? y : NEG_INF) : y;
     }
     float mb = fmaxf(x[0], x[1]);
@@ -167,10 +156,8 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
 #pragma unroll
       for (int k = 0; k < 2; ++k) p_own[k][h] = fast_exp2(x[k] - m_new);
     }
-    if constexpr (!kQuant<KVT>) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) p_oth[k][h] = dpp<kRowMirror>(p_own[k][h]);
-    }
+    for (int k = 0; k < 2; ++k) p_oth[k][h] = dpp<kRowMirror>(p_own[k][h]);
     // sum over this lane's own two tokens; the half-row mirror is added once per item
     st.l[h] = fmaf(st.l[h], alpha, p_own[0][h] + p_own[1][h]);
     st.m[h] = m_new;
@@ -180,50 +167,7 @@ __device__ __forceinline__ void process_block(const BlockBuf<KVT, D>& b, DecodeS
       for (int e = 0; e < Gm::EV; ++e) st.acc[h][e] *= alpha;
     }
   }
-  if constexpr (kQuant<KVT>) {
-    // fold the V scale of each token into its probability (the mirror delivers the
-    // other half-row's already scaled values); invalid tokens stay exactly 0
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        p_own[k][h] = valid_k[k] ? p_own[k][h] * b.vs[k] : 0.0f;
-        p_oth[k][h] = dpp<kRowMirror>(p_own[k][h]);
-      }
-  }
   // ---- V: the row's four tokens (own set 0, other set 0, own set 1, other set 1)
-  if constexpr (kQuant<KVT>) {
-    // Token pairs (own, other) of each set: per head dim, the two tokens' values form
-    // one bf16 pair (the codes are exact in bf16), the two probabilities another
-    // (rounded once to bf16), and one dot2 does both multiply-adds in fp32.
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      float va[Gm::EV], vb[Gm::EV];
-      const bool ok_a = !MASKED || tok_v[2 * k] < b.nvalid;
-      const bool ok_b = !MASKED || tok_v[2 * k + 1] < b.nvalid;
-#pragma unroll
-      for (int w = 0; w < Gm::VW; ++w) {
-        const uint32_t ya = ok_a ? b.v[2 * k][w] : 0u;  // invalid tokens: exact zeros
-        const uint32_t yb = ok_b ? b.v[2 * k + 1][w] : 0u;
-        q8x2_to_f32<KVT>(ya, false, va[4 * w], va[4 * w + 1]);
-        q8x2_to_f32<KVT>(ya, true, va[4 * w + 2], va[4 * w + 3]);
-        q8x2_to_f32<KVT>(yb, false, vb[4 * w], vb[4 * w + 1]);
-        q8x2_to_f32<KVT>(yb, true, vb[4 * w + 2], vb[4 * w + 3]);
-      }
-      uint32_t vp[Gm::EV];
-#pragma unroll
-      for (int e = 0; e < Gm::EV; ++e) vp[e] = pack_bf16_exact(va[e], vb[e]);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const bf2 pp = bf16x2_rne(p_own[k][h], p_oth[k][h]);
-#pragma unroll
-        for (int e = 0; e < Gm::EV; ++e)
-          st.acc[h][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf2, vp[e]),
-                                                         st.acc[h][e], false);
-      }
-    }
-    return;
-  }
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     const bool valid_v = !MASKED || tok_v[x] < b.nvalid;
@@ -367,6 +311,7 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
                                              const char* krow_new = nullptr,
                                              const char* vrow_new = nullptr) {
   using Gm = Geom<KVT, D>;
+  static_assert(!kQuant<KVT>, "quantised pools take the matrix-core item");
   constexpr float NEG_INF = -__builtin_huge_valf();
   const int t0 = split * a.split_tokens;
   const int t1 = min(L, t0 + a.split_tokens);
@@ -392,12 +337,9 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
   }
 
   const int64_t blk_bytes = (int64_t)kBlockSize * a.hkv * Gm::ROW;
-  uint32_t kofs[2], vofs[4], sofs[2];
+  uint32_t kofs[2], vofs[4];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    kofs[k] = (uint32_t)((tok_k[k] * a.hkv + g) * Gm::ROW + t8 * 16);
-    sofs[k] = (uint32_t)(tok_k[k] * a.hkv + g);
-  }
+  for (int k = 0; k < 2; ++k) kofs[k] = (uint32_t)((tok_k[k] * a.hkv + g) * Gm::ROW + t8 * 16);
 #pragma unroll
   for (int x = 0; x < 4; ++x) vofs[x] = (uint32_t)((tok_v[x] * a.hkv + g) * Gm::ROW + cv * Gm::VB);
 
@@ -426,16 +368,6 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
 #pragma unroll
     for (int x = 0; x < 4; ++x)
       load_dwords<Gm::VW>(tok_v[x] == pnew ? vrow_new + cv * Gm::VB : vb + vofs[x], b.v[x]);
-    if constexpr (kQuant<KVT>) {
-      const int64_t sb = bid * kBlockSize * a.hkv;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        b.ks[k] = a.kscale[sb + sofs[k]];
-        b.vs[k] = a.vscale[sb + sofs[k]];
-      }
-    } else {
-      b.ks[0] = b.ks[1] = b.vs[0] = b.vs[1] = 1.0f;
-    }
   };
 
   DecodeState<KVT, D, G> st;
@@ -454,7 +386,7 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
   };
 
   // ring of NB block buffers: block j + NB - 1 is requested before block j is used
-  constexpr int NB = RingDepth<KVT, G>::value;
+  constexpr int NB = RingDepth<G>::value;
   BlockBuf<KVT, D> ring[NB];
   if (nblk > 0) {
     // every request is unconditional (past the last block, the last block is requested
@@ -517,10 +449,16 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
 // item_partial's output (lane c < 16: dims c*D/16 .. of every head), so the merges
 // downstream are shared. Probabilities enter the PV product as bf16: for bf16 pools as a
 // hi + lo pair (two products, P exact to ~2^-17, like the fp32 P of item_partial); for
-// quantised pools once rounded, with the V scale folded in (as item_partial does).
-template <int KVT>
+// quantised pools once rounded, with the V scale folded in.
+// Which item body a (pool dtype, group size) takes, in every schedule alike so that
+// the schedules keep giving identical bits. On calls that stream from HBM the
+// dot-product body keeps more bytes in flight per wave for bf16 pools with small
+// query groups (G <= 4: 5.8 against 5.5 TB/s at 32/8 heads, 6.3 against 6.2 at 8/8);
+// from G 8 on the matrix cores win (5.0 against 4.9 at 64/8), and at G 6 they cut the
+// latency-bound small-batch call (13.9 against 16.2 us at 8 x 12/2 heads).
+template <int KVT, int G>
 struct MmaPath {
-  static constexpr bool value = KVT == kBF16 || kQuant<KVT>;
+  static constexpr bool value = kQuant<KVT> || (KVT == kBF16 && G > 4);
 };
 constexpr float kMmaLazyMax = 8.0f;  // log2 headroom of the lazily moved reference max
 // blocks in flight per wave: as many as fit in 256 registers with the wave count the
@@ -814,7 +752,7 @@ __device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split
   using Gm = Geom<KVT, D>;
   float o[G][Gm::EV], lse2[G];
   int nsplit;
-  if constexpr (MmaPath<KVT>::value) {
+  if constexpr (MmaPath<KVT, G>::value) {
     __shared__ float stage[kWaves][G][D];
     MmaIn<D> in;
     load_mma_inputs<ElemBytes<KVT>::value, D, G>(a, s, split, g, lane, in);
@@ -929,7 +867,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* wave_sums, int& 
 }
 
 template <int KVT, int D, int G, int QT>
-__global__ void __launch_bounds__(64 * kWaves, MmaPath<KVT>::value ? 2 : 1)
+__global__ void __launch_bounds__(64 * kWaves, (MmaPath<KVT, G>::value) ? 2 : 1)
     decode_compact_kernel(SplitArgs a) {
   __shared__ int cum[kMaxCompactSeqs + 1];  // cum[s] = splits of sequences before s
   __shared__ int wave_sums[kWaves];
@@ -1182,7 +1120,7 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   // the item's inputs are requested before its context length is known
   ItemIn<KVT, D, G> in;
   MmaIn<D> min_;
-  if constexpr (MmaPath<KVT>::value)
+  if constexpr (MmaPath<KVT, G>::value)
     load_mma_inputs<ElemBytes<KVT>::value, D, G>(a, s, split, g, lane, min_);
   else load_item_inputs<KVT, D, G, QT>(a, s, split, g, lane, in);
   const char* krow_new = nullptr;
@@ -1208,7 +1146,7 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   const int ngroups = (nsplit + NW - 1) / NW;
   if (c >= ngroups) return;  // uniform over the workgroup, before any barrier
   float o[G][Gm::EV], lse2[G];
-  if constexpr (MmaPath<KVT>::value)
+  if constexpr (MmaPath<KVT, G>::value)
     item_partial_mma<KVT, D, G>(a, min_, split, g, L, lane, o, lse2, part_o[wave], krow_new,
                                 vrow_new);
   else
