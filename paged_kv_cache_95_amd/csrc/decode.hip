@@ -9,9 +9,10 @@
 // the workspace; a second, small launch merges them.
 //
 // Work item = (sequence s, split i, KV head g) = one wavefront, which serves all G
-// query heads of the group, so every K/V byte is read once; the KV heads of one split
-// are neighbouring work items, so a pool block (all KV heads of 16 tokens) is fetched
-// by one workgroup at about the same time. Two item bodies exist: the dot-product one
+// query heads of the group, so every K/V byte is read once; in the persistent and
+// plain-grid schedules the KV heads of one split are neighbouring work items, so a
+// pool block (all KV heads of 16 tokens) is fetched by one workgroup at about the same
+// time. Two item bodies exist: the dot-product one
 // described here (fp32 pools, and bf16 pools with G <= 4) and the matrix-core one
 // further down (bf16 pools with G > 4, FP8, INT8).
 // Dot-product item, lane = 16r + 8h + t (DPP row r, half h):
@@ -528,13 +529,31 @@ struct MmaBuf {
   int nvalid;
 };
 
+// Issue fairness between the two waves of a SIMD in the single-launch kernel (eight
+// waves, wave w and w + 4 on one SIMD, equal work). The SIMD's arbiter favours the
+// older wave, so without this wave w finished its split ~12 us before wave w + 4 on
+// the 64 x 8192 FP8 decode and the SIMD ran its last stretch with one wave, exposing
+// load latency. Each wave posts its block count in LDS; the one behind its partner
+// raises its issue priority. Scheduling only: the arithmetic is unchanged.
+__device__ __forceinline__ void balance_issue(int* progress, int done) {
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_store(&progress[wave], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // uniform, so that the branch is a scalar one (s_setprio ignores the exec mask)
+  const int other = __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(&progress[wave ^ 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+  if (done < other) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 template <int KVT, int D, int G, int NB = MmaRing<KVT>::value>
 __device__ __forceinline__ void item_partial_mma(const SplitArgs& a, const MmaIn<D>& in,
                                                  int split, int g, int L, int lane,
                                                  float (&o)[G][D / 16], float (&lse2)[G],
                                                  float (&sw)[G][D],
                                                  const char* krow_new = nullptr,
-                                                 const char* vrow_new = nullptr) {
+                                                 const char* vrow_new = nullptr,
+                                                 int* progress = nullptr) {
   using Bf = MmaBuf<KVT, D>;
   constexpr int E = Bf::E;
   constexpr int ROW = D * E;
@@ -708,12 +727,14 @@ __device__ __forceinline__ void item_partial_mma(const SplitArgs& a, const MmaIn
     for (int p = 0; p < NB - 1; ++p) load(ring[p], min(p, nblk - 1));
     int j0 = 0;
     for (; j0 + NB <= nblk; j0 += NB) {
+      if (progress != nullptr) balance_issue(progress, j0);
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         load(ring[(u + NB - 1) % NB], min(j0 + u + NB - 1, nblk - 1));
         process(ring[u]);
       }
     }
+    if (progress != nullptr) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u)
       if (j0 + u < nblk) process(ring[u]);
@@ -1111,12 +1132,20 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   __shared__ float part_o[NW][G][D];
   __shared__ float part_lse[NW][G];
   __shared__ unsigned arrival;
+  __shared__ int progress[NW];  // blocks done per wave (issue fairness, see balance_issue)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = (int)(blockIdx.x % a.hkv);
-  const int rest = (int)(blockIdx.x / a.hkv);
+  // KV head slowest: consecutive workgroups go to different XCDs, so every XCD gets
+  // the same mix of heads (with the head fastest, an XCD would only see heads
+  // congruent to its index, and the FP8 64 x 8192 decode ran ~15% longer on KV head 1
+  // than on head 0, which left the XCDs holding head 1 finishing last)
+  const int per_head = a.num_seqs * a.max_chunks;
+  const int g = (int)blockIdx.x / per_head;
+  const int rest = (int)blockIdx.x - g * per_head;
   const int c = rest % a.max_chunks;
   const int s = rest / a.max_chunks;
   const int split = c * NW + wave;
+  static_assert(NW == 8, "balance_issue pairs wave w with w + 4");
+  if (lane == 0) progress[wave] = 0;
   // the item's inputs are requested before its context length is known
   ItemIn<KVT, D, G> in;
   MmaIn<D> min_;
@@ -1148,7 +1177,7 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   float o[G][Gm::EV], lse2[G];
   if constexpr (MmaPath<KVT, G>::value)
     item_partial_mma<KVT, D, G>(a, min_, split, g, L, lane, o, lse2, part_o[wave], krow_new,
-                                vrow_new);
+                                vrow_new, progress);
   else
     item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2, krow_new, vrow_new);
   if (lane < 16) {
