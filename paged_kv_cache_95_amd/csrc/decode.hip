@@ -12,9 +12,9 @@
 // query heads of the group, so every K/V byte is read once; in the persistent and
 // plain-grid schedules the KV heads of one split are neighbouring work items, so a
 // pool block (all KV heads of 16 tokens) is fetched by one workgroup at about the same
-// time. Two item bodies exist: the dot-product one
-// described here (fp32 pools, and bf16 pools with G <= 4) and the matrix-core one
-// further down (bf16 pools with G > 4, FP8, INT8).
+// time. Two item bodies exist: the dot-product one described here (fp32 pools, and
+// bf16 pools with G <= 4) and the matrix-core one further down (bf16 pools with G > 4,
+// FP8, INT8).
 // Dot-product item, lane = 16r + 8h + t (DPP row r, half h):
 //
 //   K side  the 8 lanes of a half-row share one token and each loads 16-byte chunks
@@ -452,11 +452,12 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
 // hi + lo pair (two products, P exact to ~2^-17, like the fp32 P of item_partial); for
 // quantised pools once rounded, with the V scale folded in.
 // Which item body a (pool dtype, group size) takes, in every schedule alike so that
-// the schedules keep giving identical bits. On calls that stream from HBM the
-// dot-product body keeps more bytes in flight per wave for bf16 pools with small
-// query groups (G <= 4: 5.8 against 5.5 TB/s at 32/8 heads, 6.3 against 6.2 at 8/8);
-// from G 8 on the matrix cores win (5.0 against 4.9 at 64/8), and at G 6 they cut the
-// latency-bound small-batch call (13.9 against 16.2 us at 8 x 12/2 heads).
+// the schedules keep giving identical bits. Measured on bf16 calls that stream from
+// HBM (256 sequences, contexts 1K-32K), the dot-product body, whose K loads cover
+// whole 128-byte lines per instruction, is faster for small query groups (G = 4: 5.8
+// against 5.5 TB/s; G = 1: 6.3 against 6.2), equal at G = 6, and slower at G = 8 (4.9
+// against 5.0); at G = 6 the matrix cores also cut the latency-bound small-batch
+// call (13.9 against 16.2 us at 8 sequences x 12/2 heads).
 template <int KVT, int G>
 struct MmaPath {
   static constexpr bool value = kQuant<KVT> || (KVT == kBF16 && G > 4);
