@@ -127,6 +127,26 @@ def test_both_schedules_give_identical_bits(dev):
         assert torch.equal(o1[0], out[b]), b
 
 
+@pytest.mark.parametrize("kv,Hq,Hkv", [("bf16", 8, 2), ("bf16", 12, 2), ("fp8", 12, 2),
+                                       ("int8", 16, 2)])
+def test_each_item_body_gives_identical_bits_in_both_schedules(dev, kv, Hq, Hkv):
+    """The item body (dot-product for bf16 with G <= 4, matrix cores for bf16 with
+    G > 4 and for FP8 / INT8) is chosen per (dtype, G), the same in both schedules: a
+    batch on the persistent split + merge launches and each sequence alone on the
+    single-launch kernel give the same bits."""
+    case = W.random_case(13, B=48, Hq=Hq, Hkv=Hkv, D=128, kv_dtype=kv, lmin=1, lmax=1500)
+    s = Setup(case, dev)
+    ws = pa.decode_workspace(48, Hq, Hkv, 128, 1500, 16, device=dev)
+    out = pa.decode(s.q, s.pool, s.bt, s.ctx, case.scale, max_context_len=1500,
+                    split_tokens=16, workspace=ws)  # 48 x 2 x 12 groups: split + merge
+    torch.cuda.synchronize()
+    assert max_err(out, s.oracle()) <= TOL[kv]
+    for b in [0, 1, int(np.argmin(case.context_lens)), int(np.argmax(case.context_lens))]:
+        o1 = pa.decode(s.q[b:b + 1], s.pool, s.bt[b:b + 1], s.ctx[b:b + 1], case.scale,
+                       max_context_len=1500, split_tokens=16, workspace=ws)
+        assert torch.equal(o1[0], out[b]), b
+
+
 def test_poisoned_slots_and_tables_do_not_leak(dev):
     case = W.random_case(11, B=5, Hq=8, Hkv=2, D=128, lmin=3, lmax=500)
     clean = Setup(case, dev, poison=False)
