@@ -1146,7 +1146,8 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   const int s = rest / a.max_chunks;
   const int split = c * NW + wave;
   static_assert(NW == 8, "balance_issue pairs wave w with w + 4");
-  if (lane == 0) progress[wave] = 0;
+  if (lane == 0)
+    __hip_atomic_store(&progress[wave], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   // the item's inputs are requested before its context length is known
   ItemIn<KVT, D, G> in;
   MmaIn<D> min_;
