@@ -547,7 +547,9 @@ __device__ __forceinline__ void balance_issue(int* progress, int done) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-template <int KVT, int D, int G, int NB = MmaRing<KVT>::value>
+// OUT_REGS = false: the normalised result is left in sw only ([G][D], the layout the
+// single-launch kernel merges from), and o is not written.
+template <int KVT, int D, int G, int NB = MmaRing<KVT>::value, bool OUT_REGS = true>
 __device__ __forceinline__ void item_partial_mma(const SplitArgs& a, const MmaIn<D>& in,
                                                  int split, int g, int L, int lane,
                                                  float (&o)[G][D / 16], float (&lse2)[G],
@@ -759,7 +761,7 @@ __device__ __forceinline__ void item_partial_mma(const SplitArgs& a, const MmaIn
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     lse2[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lse), h));
-    if (lane < 16) {
+    if (OUT_REGS && lane < 16) {
 #pragma unroll
       for (int e = 0; e < PS; ++e) o[h][e] = sw[h][PS * lane + e];
     }
@@ -1201,20 +1203,23 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   const int ngroups = (nsplit + NW - 1) / NW;
   if (c >= ngroups) return;  // uniform over the workgroup, before any barrier
   float o[G][Gm::EV], lse2[G];
-  if constexpr (MmaPath<KVT, G>::value)
-    item_partial_mma<KVT, D, G>(a, min_, split, g, L, lane, o, lse2, part_o[wave], krow_new,
-                                vrow_new, progress);
-  else
+  if constexpr (MmaPath<KVT, G>::value) {
+    // the item leaves its result in part_o[wave] itself
+    item_partial_mma<KVT, D, G, MmaRing<KVT>::value, false>(a, min_, split, g, L, lane, o, lse2,
+                                                            part_o[wave], krow_new, vrow_new,
+                                                            progress);
+  } else {
     item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2, krow_new, vrow_new);
-  if (lane < 16) {
+    if (lane < 16) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < Gm::EV; ++e) part_o[wave][h][lane * Gm::EV + e] = o[h][e];
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) part_lse[wave][h] = lse2[h];
+        for (int e = 0; e < Gm::EV; ++e) part_o[wave][h][lane * Gm::EV + e] = o[h][e];
     }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) part_lse[wave][h] = lse2[h];
   }
   __syncthreads();
   const int t = threadIdx.x;
