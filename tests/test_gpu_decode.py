@@ -147,6 +147,24 @@ def test_each_item_body_gives_identical_bits_in_both_schedules(dev, kv, Hq, Hkv)
         assert torch.equal(o1[0], out[b]), b
 
 
+def test_hundreds_of_groups_in_one_launch(dev):
+    """Three 60000-token contexts at split 16: one sequence alone runs the single-launch
+    kernel with 469 groups exchanging partials (the last arrival merges them in steps
+    of sixteen); the batch of three (1407 groups) runs the persistent schedule. Both
+    match the oracle and give the same bits."""
+    case = W.random_case(14, B=3, Hq=8, Hkv=1, D=128, lmin=60000, lmax=60000)
+    s = Setup(case, dev)
+    ws = pa.decode_workspace(3, 8, 1, 128, 60000, 16, device=dev)
+    out = pa.decode(s.q, s.pool, s.bt, s.ctx, case.scale, max_context_len=60000,
+                    split_tokens=16, workspace=ws)
+    torch.cuda.synchronize()
+    assert max_err(out, s.oracle()) <= TOL["bf16"]
+    for b in range(3):
+        o1 = pa.decode(s.q[b:b + 1], s.pool, s.bt[b:b + 1], s.ctx[b:b + 1], case.scale,
+                       max_context_len=60000, split_tokens=16, workspace=ws)
+        assert torch.equal(o1[0], out[b]), b
+
+
 def test_poisoned_slots_and_tables_do_not_leak(dev):
     case = W.random_case(11, B=5, Hq=8, Hkv=2, D=128, lmin=3, lmax=500)
     clean = Setup(case, dev, poison=False)
