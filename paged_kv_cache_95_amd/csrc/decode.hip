@@ -227,6 +227,15 @@ struct SplitArgs {
   bool out_aligned;  // same for out
 };
 
+// Uniform read of call metadata that nothing writes during the launch, through the
+// constant address space, so it is a scalar load (SGPR result, lgkmcnt): the vector
+// loads issued around it are not waited for, and no readfirstlane is needed.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  typedef const __attribute__((address_space(4))) T cT;
+  return *(cT*)(uintptr_t)p;
+}
+
 // Context length as the kernels use it: clamped to the host bound, so a longer value
 // (a contract violation) cannot index past the sequence's workspace rows or its
 // block-table row; its output is then unspecified.
@@ -1150,7 +1159,9 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(SplitArgs a
 // KV head) counter; the last group to arrive merges them (level 2) and writes out,
 // then returns the counter to zero. This replaces the merge launch and its dependent
 // loads, which dominate the time of such small calls.
-template <int KVT, int D, int G, int QT>
+// STEP: a decode step (knew / vnew / slots set); a separate instantiation so that its
+// loads are issued with the others, not behind a branch.
+template <int KVT, int D, int G, int QT, bool STEP>
 __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitArgs a) {
   using Gm = Geom<KVT, D>;
   constexpr int NW = kGroupSplits;
@@ -1160,6 +1171,16 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   __shared__ float part_lse[NW][G];
   __shared__ unsigned arrival;
   __shared__ int progress[NW];  // blocks done per wave (issue fairness, see balance_issue)
+  // Every kernel argument the launch uses, loaded up front: without this the compiler
+  // loads them region by region behind divergent branches, and each region waited
+  // for its own round trip to the argument segment before its memory requests.
+  asm volatile("" ::"s"(a.kpool), "s"(a.vpool), "s"(a.q), "s"(a.block_tables),
+               "s"(a.context_lens), "s"(a.slots), "s"(a.knew), "s"(a.vnew), "s"(a.out),
+               "s"(a.max_blocks_per_seq), "s"(a.hkv), "s"(a.max_chunks), "s"(a.num_seqs),
+               "s"(a.q_st), "s"(a.q_sh), "s"(a.max_context_len), "s"(a.split_tokens),
+               "s"(a.num_blocks), "s"(a.knew_st), "s"(a.knew_sh), "s"(a.vnew_st),
+               "s"(a.vnew_sh), "s"(a.counters), "s"(a.ws_o), "s"(a.ws_lse),
+               "s"(a.scale_log2), "s"((int)a.q_aligned), "s"((int)a.out_aligned));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // KV head slowest: consecutive workgroups go to different XCDs, so every XCD gets
   // the same mix of heads (with the head fastest, an XCD would only see heads
@@ -1174,34 +1195,49 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   static_assert(NW == 8, "balance_issue pairs wave w with w + 4");
   if (lane == 0)
     __hip_atomic_store(&progress[wave], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  // the item's inputs are requested before its context length is known
+  // the context length and the step's slot, then the item's inputs: every request is
+  // out before the first of them is used (one round trip for all)
+  const int L_raw = ld_uniform(a.context_lens + s);
+  int64_t slot = STEP ? ld_uniform(a.slots + s) : -1;
   ItemIn<KVT, D, G> in;
   MmaIn<D> min_;
   if constexpr (MmaPath<KVT, G>::value)
     load_mma_inputs<ElemBytes<KVT>::value, D, G>(a, s, split, g, lane, min_);
   else load_item_inputs<KVT, D, G, QT>(a, s, split, g, lane, in);
+  asm volatile("" ::"s"(L_raw), "s"(slot));  // the first use of either value
+  const int L = min(L_raw, a.max_context_len);
+  // Decode step: every wave reads the new K/V row from the input, not from the pool,
+  // and group 0 of (s, g) copies it into the pool (waves 0 and 1, 16 bytes per lane).
+  // The copy's load goes out with the item's inputs and its store after the item:
+  // nothing in this launch reads that pool slot, and the item does not wait for it.
   const char* krow_new = nullptr;
   const char* vrow_new = nullptr;
-  if (a.knew != nullptr) {
-    // decode step: group 0 of (s, g) stores the new K/V row (waves 0 and 1, 16 bytes
-    // per lane); every wave reads that row from the input, not from the pool
-    const int64_t slot = a.slots[s];
-    if (slot >= 0) {
-      krow_new = a.knew + ((int64_t)s * a.knew_st + (int64_t)g * a.knew_sh) * Gm::E;
-      vrow_new = a.vnew + ((int64_t)s * a.vnew_st + (int64_t)g * a.vnew_sh) * Gm::E;
-      if (c == 0 && wave < 2 && lane < Gm::NCH && slot < a.num_blocks * kBlockSize) {
-        const int64_t off = (slot / kBlockSize) * kBlockSize * a.hkv * Gm::ROW +
-                            ((slot % kBlockSize) * a.hkv + g) * Gm::ROW + lane * 16;
-        const char* src = (wave == 0 ? krow_new : vrow_new) + lane * 16;
-        char* dst = const_cast<char*>(wave == 0 ? a.kpool : a.vpool) + off;
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-      }
-    }
+  const bool copier = STEP && c == 0 && wave < 2 && lane < Gm::NCH;
+  uint4 new_row = make_uint4(0, 0, 0, 0);
+  if constexpr (STEP) {
+    krow_new = a.knew + ((int64_t)s * a.knew_st + (int64_t)g * a.knew_sh) * Gm::E;
+    vrow_new = a.vnew + ((int64_t)s * a.vnew_st + (int64_t)g * a.vnew_sh) * Gm::E;
+    // every lane loads (a chunk of its wave's row: in bounds), so no branch separates
+    // this load from the others
+    static_assert((Gm::NCH & (Gm::NCH - 1)) == 0, "chunks per row: a power of two");
+    new_row = *reinterpret_cast<const uint4*>(((wave & 1) ? vrow_new : krow_new) +
+                                              (lane & (Gm::NCH - 1)) * 16);
   }
-  const int L = clamped_len(a, s);
+  if (slot < 0) krow_new = vrow_new = nullptr;  // no new row: the pool holds the context
+  auto copy_new_row = [&]() {
+    if (copier && slot >= 0 && slot < a.num_blocks * kBlockSize) {
+      const int64_t off = (slot / kBlockSize) * kBlockSize * a.hkv * Gm::ROW +
+                          ((slot % kBlockSize) * a.hkv + g) * Gm::ROW + lane * 16;
+      char* dst = const_cast<char*>(wave == 0 ? a.kpool : a.vpool) + off;
+      *reinterpret_cast<uint4*>(dst) = new_row;
+    }
+  };
   const int nsplit = num_splits(L, a.split_tokens);
   const int ngroups = (nsplit + NW - 1) / NW;
-  if (c >= ngroups) return;  // uniform over the workgroup, before any barrier
+  if (c >= ngroups) {  // uniform over the workgroup, before any barrier
+    copy_new_row();
+    return;
+  }
   float o[G][Gm::EV], lse2[G];
   if constexpr (MmaPath<KVT, G>::value) {
     // the item leaves its result in part_o[wave] itself
@@ -1217,6 +1253,7 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
         for (int e = 0; e < Gm::EV; ++e) part_o[wave][h][lane * Gm::EV + e] = o[h][e];
     }
   }
+  copy_new_row();
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) part_lse[wave][h] = lse2[h];
@@ -1323,7 +1360,12 @@ static int launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, const 
   }
   static_assert(kFusedMaxWorkgroups <= kDecodeCounters, "one counter per (sequence, KV head)");
   if (fused_groups <= kFusedMaxWorkgroups) {
-    decode_fused_kernel<KVT, D, G, QT><<<(unsigned)fused_groups, 64 * kGroupSplits, 0, stream>>>(sa);
+    if (sa.knew != nullptr)
+      decode_fused_kernel<KVT, D, G, QT, true><<<(unsigned)fused_groups, 64 * kGroupSplits, 0,
+                                                 stream>>>(sa);
+    else
+      decode_fused_kernel<KVT, D, G, QT, false><<<(unsigned)fused_groups, 64 * kGroupSplits, 0,
+                                                  stream>>>(sa);
     return PA_OK;
   }
   const int64_t items = (int64_t)a.num_seqs * a.max_splits * pool.kv_heads;
