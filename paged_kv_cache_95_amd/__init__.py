@@ -142,6 +142,8 @@ class KVPool:
             _need(k_scale.dtype == torch.float32 and k_scale.shape == k.shape[:3]
                   and k_scale.is_contiguous() and v_scale.is_contiguous()
                   and v_scale.shape == k.shape[:3], "scales must be fp32 [nb, bs, Hkv]")
+        _need(all(t.device == k.device for t in (v, k_scale, v_scale) if t is not None),
+              "pool tensors must be on one device")
         self.num_blocks, self.block_size, self.kv_heads, self.head_dim = k.shape
         self._struct = _Pool(k.data_ptr(), v.data_ptr(),
                              k_scale.data_ptr() if k_scale is not None else 0,
@@ -183,6 +185,7 @@ def store_kv(pool, k, v, slot_mapping):
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1
           and slot_mapping.shape[0] == k.shape[0] and slot_mapping.is_contiguous(),
           "slot_mapping must be contiguous int64 [T]")
+    _one_device(k, v, slot_mapping, pool.k)
     _check(lib().pa_store_kv(pool.struct, _ptr(k), _ptr(v), _DTYPE_CODE[k.dtype], k.shape[0],
                              ks[0], ks[1], vs[0], vs[1], _ptr(slot_mapping), _stream()),
            "pa_store_kv")
@@ -208,6 +211,9 @@ def rope_store_kv(pool, q, k, v, positions, cos_table, sin_table, slot_mapping, 
     if q_out is None:
         q_out = torch.empty((T,) + tuple(q.shape[1:]), dtype=q.dtype, device=q.device)
     qo = _rows3(q_out, "q_out")
+    _need(tuple(q_out.shape) == tuple(q.shape) and q_out.dtype == q.dtype,
+          "q_out must have q's shape and dtype")
+    _one_device(q, q_out, k, v, positions, cos_table, sin_table, slot_mapping, pool.k)
     _check(lib().pa_rope_store_kv(pool.struct, _ptr(q), qs[0], qs[1], q.shape[1], _ptr(q_out),
                                   qo[0], qo[1], _ptr(k), _ptr(v), _DTYPE_CODE[k.dtype], T, ks[0],
                                   ks[1], vs[0], vs[1], _ptr(positions), _ptr(cos_table),
@@ -224,6 +230,7 @@ def copy_blocks(pool, src_blocks, dst_blocks):
         _need(t.dtype == torch.int32 and t.dim() == 1 and t.is_contiguous(),
               "block lists must be contiguous int32 [n]")
     _need(src_blocks.shape == dst_blocks.shape, "src/dst lengths differ")
+    _one_device(src_blocks, dst_blocks, pool.k)
     _check(lib().pa_copy_blocks(pool.struct, _ptr(src_blocks), _ptr(dst_blocks),
                                 src_blocks.shape[0], _stream()), "pa_copy_blocks")
 
@@ -309,11 +316,31 @@ def decode_workspace(num_seqs, q_heads, kv_heads, head_dim, max_context_len, spl
     return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
 
 
-def _meta(block_tables, context_lens):
+def _meta(block_tables, context_lens, num_seqs):
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
           and block_tables.is_contiguous(), "block_tables must be contiguous int32 [B, maxb]")
     _need(context_lens.dtype == torch.int32 and context_lens.dim() == 1
           and context_lens.is_contiguous(), "context_lens must be contiguous int32 [B]")
+    _need(block_tables.shape[0] >= num_seqs,
+          f"block_tables has {block_tables.shape[0]} rows for {num_seqs} sequences")
+    _need(context_lens.shape[0] >= num_seqs,
+          f"context_lens has {context_lens.shape[0]} entries for {num_seqs} sequences")
+
+
+def _rows_like(q, out, pool, name="out"):
+    """q [N, Hq, head_dim] of the pool's head_dim; out of q's shape and dtype."""
+    _need(q.dim() == 3 and q.shape[2] == pool.head_dim,
+          f"q must be [tokens, q_heads, {pool.head_dim}] (the pool's head_dim)")
+    _need(tuple(out.shape) == tuple(q.shape), f"{name} must have q's shape {tuple(q.shape)}")
+    _need(out.dtype == q.dtype, f"{name} must have q's dtype {q.dtype}")
+
+
+def _one_device(*tensors):
+    """Every tensor argument of a kernel call lives on the same GPU (and so does the
+    pool): the kernels take raw device pointers."""
+    devs = {t.device for t in tensors if t is not None}
+    _need(len(devs) == 1 and next(iter(devs)).type == "cuda",
+          f"all tensors must be on one CUDA device (got {sorted(map(str, devs))})")
 
 
 def decode(q, pool, block_tables, context_lens, scale, max_context_len=None, split_tokens=0,
@@ -322,13 +349,16 @@ def decode(q, pool, block_tables, context_lens, scale, max_context_len=None, spl
     max_context_len: host-side bound of context_lens (default: the block table's
     capacity; no device sync). workspace: optional preallocated uint8 tensor, zero-filled
     before its first use (decode_workspace()); reusing one keeps the call allocation-free."""
-    _meta(block_tables, context_lens)
+    qs = _rows3(q, "q")
     B, Hq, D = q.shape
+    _meta(block_tables, context_lens, B)
     if max_context_len is None:
         max_context_len = block_tables.shape[1] * pool.block_size
     if out is None:
         out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
-    qs, os_ = _rows3(q, "q"), _rows3(out, "out")
+    os_ = _rows3(out, "out")
+    _rows_like(q, out, pool)
+    _one_device(q, out, block_tables, context_lens, workspace, pool.k)
     need = decode_workspace_bytes(B, Hq, pool.kv_heads, D, max_context_len, split_tokens)
     if need and workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
@@ -346,8 +376,9 @@ def decode_step(q, pool, k_new, v_new, slot_mapping, block_tables, context_lens,
     """One decode step: store row s of k_new / v_new [B, kv_heads, head_dim] at
     slot_mapping[s] (int64; negative = no new token), then attend as decode(); the same
     result as store_kv() followed by decode(), in one launch for small batches."""
-    _meta(block_tables, context_lens)
+    qs = _rows3(q, "q")
     B, Hq, D = q.shape
+    _meta(block_tables, context_lens, B)
     ks, vs = _rows3(k_new, "k_new"), _rows3(v_new, "v_new")
     _need(k_new.shape == v_new.shape and k_new.shape == (B, pool.kv_heads, pool.head_dim),
           "k_new/v_new shape [B, kv_heads, head_dim]")
@@ -359,7 +390,9 @@ def decode_step(q, pool, k_new, v_new, slot_mapping, block_tables, context_lens,
         max_context_len = block_tables.shape[1] * pool.block_size
     if out is None:
         out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
-    qs, os_ = _rows3(q, "q"), _rows3(out, "out")
+    os_ = _rows3(out, "out")
+    _rows_like(q, out, pool)
+    _one_device(q, out, k_new, v_new, slot_mapping, block_tables, context_lens, workspace, pool.k)
     need = decode_workspace_bytes(B, Hq, pool.kv_heads, D, max_context_len, split_tokens)
     if need and workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
@@ -394,18 +427,22 @@ def varlen_prefill(q, cu_seqlens, pool, block_tables, context_lens, scale, max_q
     """Varlen causal prefill: q [T, Hq, D] with chunks cu_seqlens [B+1] -> out [T, Hq, D].
     split_tokens: keys per work item (0 = library default); workspace: optional
     preallocated uint8 tensor (varlen_prefill_workspace())."""
-    _meta(block_tables, context_lens)
     _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1
-          and cu_seqlens.is_contiguous(), "cu_seqlens must be contiguous int32 [B+1]")
+          and cu_seqlens.is_contiguous() and cu_seqlens.shape[0] >= 1,
+          "cu_seqlens must be contiguous int32 [B+1]")
+    qs = _rows3(q, "q")
     T, Hq, D = q.shape
     B = cu_seqlens.shape[0] - 1
+    _meta(block_tables, context_lens, B)
     if max_context_len is None:
         max_context_len = block_tables.shape[1] * pool.block_size
     if max_q_len is None:
         max_q_len = min(T, max_context_len)
     if out is None:
         out = torch.empty((T, Hq, D), dtype=q.dtype, device=q.device)
-    qs, os_ = _rows3(q, "q"), _rows3(out, "out")
+    os_ = _rows3(out, "out")
+    _rows_like(q, out, pool)
+    _one_device(q, out, cu_seqlens, block_tables, context_lens, workspace, pool.k)
     need = varlen_prefill_workspace_bytes(T, Hq, D, max_context_len, split_tokens)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

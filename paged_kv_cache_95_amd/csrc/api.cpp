@@ -181,6 +181,15 @@ int pa_store_kv(const pa_kv_pool_t* pool, const void* k, const void* v, int32_t 
 
 namespace {
 
+// workspace: [arrival counters, fixed 4 KiB][o: num_seqs, q_heads, max_splits, D][lse];
+// nullptr when the call needs none (every context fits one split).
+void bind_decode_workspace(pa::DecodeArgs* a, void* workspace) {
+  a->counters = workspace ? (unsigned*)workspace : nullptr;
+  a->ws_o = workspace ? (float*)((char*)workspace + pa::kDecodeCounterBytes) : nullptr;
+  a->ws_lse = workspace ? a->ws_o + (size_t)a->num_seqs * a->q_heads * a->max_splits * a->head_dim
+                        : nullptr;
+}
+
 // Validation and argument block shared by pa_decode and pa_decode_step. Returns PA_OK
 // with *nothing = true when there is no sequence to decode.
 int prepare_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const void* q,
@@ -231,11 +240,8 @@ int prepare_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, c
   a->scale = scale;
   a->split_tokens = split;
   a->max_splits = max_splits;
-  // workspace: [arrival counters, fixed 4 KiB][o: num_seqs, q_heads, max_splits, D][lse]
-  a->counters = need > 0 ? (unsigned*)workspace : nullptr;
-  a->ws_o = need > 0 ? (float*)((char*)workspace + pa::kDecodeCounterBytes) : nullptr;
-  a->ws_lse = need > 0 ? a->ws_o + (size_t)num_seqs * q_heads * max_splits * pool->head_dim
-                       : nullptr;
+  a->head_dim = pool->head_dim;
+  bind_decode_workspace(a, need > 0 ? workspace : nullptr);
   return PA_OK;
 }
 

@@ -1240,6 +1240,14 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   }
   float o[G][Gm::EV], lse2[G];
   if constexpr (MmaPath<KVT, G>::value) {
+    // Every wave's progress word is written before any wave reads its partner's (the
+    // LDS may still hold an earlier workgroup's words). The wait covers LDS and scalar
+    // memory only (the scalar loads were consumed above), so the item's vector loads
+    // stay in flight; every wave of the workgroup reaches this barrier (the return
+    // above is uniform over the workgroup).
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     // the item leaves its result in part_o[wave] itself
     item_partial_mma<KVT, D, G, MmaRing<KVT>::value, false>(a, min_, split, g, L, lane, o, lse2,
                                                             part_o[wave], krow_new, vrow_new,

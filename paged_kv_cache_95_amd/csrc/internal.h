@@ -44,6 +44,7 @@ struct DecodeArgs {
   float scale;
   int split_tokens;
   int max_splits;
+  int head_dim;
   float* ws_o;    // [num_seqs, q_heads, max_splits, head_dim]
   float* ws_lse;  // [num_seqs, q_heads, max_splits]
   unsigned* counters;  // [num_seqs, kv_heads] used of kDecodeCounters, zero between calls

@@ -8,6 +8,8 @@ import torch
 
 import paged_kv_cache_95_amd as pa
 import workloads as W
+from oracle import fp8 as ofp8
+from oracle import ref
 
 from _harness import TOL, Setup, max_err
 
@@ -115,3 +117,132 @@ def test_step_graph_replay(dev):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i}"
         del junk
+
+
+@pytest.mark.parametrize("kv,split", [("bf16", 32), ("fp8", 32), ("bf16", 16)])
+def test_engine_graph_replay_with_in_place_updates(dev, kv, split):
+    """The engine pattern of a captured decode step: fixed, padded device buffers for q,
+    the new K/V rows, slot_mapping, block_tables and context_lens; the step is captured
+    once, and before each of ten replays the host writes the next token's values into
+    those buffers in place (context_lens += 1, the next slots, one of which crosses into
+    a new block every 16 steps for some sequence). Two of the eight batch entries are
+    padding: slot -1 and context length 1 on a dummy block. Every replay is checked
+    against the oracle (attention) and the whole pool against the oracle's store."""
+    rng = np.random.default_rng(70)
+    B, real, Hq, Hkv, D, nb, steps = 8, 6, 12, 2, 128, 256, 10
+    L0 = np.array([14, 30, 95, 250, 1007, 47], np.int64)          # tokens before step 0
+    maxb = int(-(-(L0.max() + steps) // 16))
+    perm = rng.permutation(nb - 1).astype(np.int32) + 1          # block 0: the dummy block
+    bt = np.full((B, maxb), -1, np.int32)
+    off = 0
+    for s in range(real):
+        n = int(-(-(L0[s] + steps) // 16))
+        bt[s, :n] = perm[off:off + n]
+        off += n
+    bt[real:, 0] = 0
+    shape = (nb, 16, Hkv, D)
+    src0_k = W.round_to_bf16(rng.standard_normal(shape, dtype=np.float32))
+    src0_v = W.round_to_bf16(rng.standard_normal(shape, dtype=np.float32))
+    if kv == "bf16":
+        pool = pa.KVPool(torch.from_numpy(src0_k).to(torch.bfloat16).to(dev),
+                         torch.from_numpy(src0_v).to(torch.bfloat16).to(dev))
+        ref_k = W.bf16_bits(src0_k)
+        ref_v = W.bf16_bits(src0_v)
+    else:
+        # the prefix goes in through the FP8 store on both sides (one row per slot)
+        pool = pa.KVPool.empty(nb, Hkv, D, "fp8", dev)
+        for t in (pool.k, pool.v):
+            t.zero_()
+        for t in (pool.k_scale, pool.v_scale):
+            t.zero_()
+        all_slots = torch.arange(nb * 16, dtype=torch.int64, device=dev)
+        pa.store_kv(pool, torch.from_numpy(src0_k.reshape(nb * 16, Hkv, D)).to(torch.bfloat16).to(dev),
+                    torch.from_numpy(src0_v.reshape(nb * 16, Hkv, D)).to(torch.bfloat16).to(dev),
+                    all_slots)
+        z = np.zeros(shape, np.uint8)
+        zs = np.zeros(shape[:3], np.float32)
+        sl = np.arange(nb * 16)
+        ref_k = ref.store_fp8_ref(z, zs, src0_k.reshape(nb * 16, Hkv, D), sl)
+        ref_v = ref.store_fp8_ref(z, zs, src0_v.reshape(nb * 16, Hkv, D), sl)
+
+    def pool_values(r):
+        if kv == "bf16":
+            return ref.bf16_bits_to_f64(r)
+        return ofp8.decode(r[0]) * r[1].astype(np.float64)[..., None]
+
+    def ref_store(r, rows, slots):
+        if kv == "bf16":
+            return ref.store_ref(r, W.bf16_bits(rows), slots)
+        return ref.store_fp8_ref(r[0], r[1], rows, slots)
+
+    def pool_matches(r):
+        if kv == "bf16":
+            return (np.array_equal(pool.k.cpu().view(torch.int16).numpy().view(np.uint16), r[0])
+                    and np.array_equal(pool.v.cpu().view(torch.int16).numpy().view(np.uint16), r[1]))
+        return (np.array_equal(pool.k.cpu().numpy(), r[0][0])
+                and np.array_equal(pool.k_scale.cpu().numpy().view(np.uint32), r[0][1].view(np.uint32))
+                and np.array_equal(pool.v.cpu().numpy(), r[1][0])
+                and np.array_equal(pool.v_scale.cpu().numpy().view(np.uint32), r[1][1].view(np.uint32)))
+
+    bf = torch.bfloat16
+    q_buf = torch.zeros((B, Hq, D), dtype=bf, device=dev)
+    kn_buf = torch.zeros((B, Hkv, D), dtype=bf, device=dev)
+    vn_buf = torch.zeros((B, Hkv, D), dtype=bf, device=dev)
+    slot_buf = torch.full((B,), -1, dtype=torch.int64, device=dev)
+    ctx_buf = torch.ones((B,), dtype=torch.int32, device=dev)
+    bt_buf = torch.from_numpy(bt).to(dev)
+    out_buf = torch.zeros((B, Hq, D), dtype=bf, device=dev)
+    maxctx = maxb * 16
+    ws = pa.decode_workspace(B, Hq, Hkv, D, maxctx, split, device=dev)
+
+    def host_step(i):
+        q = W.round_to_bf16(rng.standard_normal((B, Hq, D), dtype=np.float32))
+        kn = W.round_to_bf16(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+        vn = W.round_to_bf16(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+        ctx = np.ones(B, np.int32)
+        slots = np.full(B, -1, np.int64)
+        for s in range(real):
+            p = int(L0[s]) + i
+            ctx[s] = p + 1
+            slots[s] = int(bt[s, p // 16]) * 16 + p % 16
+        return q, kn, vn, ctx, slots
+
+    def load(hs):
+        q, kn, vn, ctx, slots = hs
+        q_buf.copy_(torch.from_numpy(q).to(bf))
+        kn_buf.copy_(torch.from_numpy(kn).to(bf))
+        vn_buf.copy_(torch.from_numpy(vn).to(bf))
+        ctx_buf.copy_(torch.from_numpy(ctx))
+        slot_buf.copy_(torch.from_numpy(slots))
+
+    def step():
+        pa.decode_step(q_buf, pool, kn_buf, vn_buf, slot_buf, bt_buf, ctx_buf, D ** -0.5,
+                       max_context_len=maxctx, split_tokens=split, out=out_buf, workspace=ws)
+
+    # capture with step 0's inputs loaded but the pool untouched: run nothing eagerly
+    hs = host_step(0)
+    load(hs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    crossed = 0
+    for i in range(steps):
+        if i > 0:
+            hs = host_step(i)
+            load(hs)
+        q, kn, vn, ctx, slots = hs
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_k = ref_store(ref_k, kn, slots)
+        ref_v = ref_store(ref_v, vn, slots)
+        assert pool_matches((ref_k, ref_v)), f"pool bytes differ after replay {i}"
+        exp = ref.decode_ref(q, pool_values(ref_k), pool_values(ref_v), bt, ctx, D ** -0.5)[0]
+        err = max_err(out_buf, exp)
+        assert err <= TOL[kv], f"replay {i}: max_abs_err {err:.3e}"
+        crossed += int(np.sum((ctx[:real] - 1) % 16 == 0))
+        junk = torch.randn(1000, device=dev).sum()                 # unrelated eager work
+        del junk
+    assert crossed >= 3                                            # block boundaries crossed

@@ -29,7 +29,7 @@ def test_varlen_mixed_config(dev):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 6, 8])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_random_shapes(dev, D, G):
     hkv = 2 if G <= 4 else 1
     case = W.random_case(300 + G * 10 + D, kind="varlen", B=6, Hq=G * hkv, Hkv=hkv, D=D,

@@ -89,7 +89,7 @@ def test_store_fp8_bitexact(dev, D, src):
     x[5, 0] = 0.0                                        # zero row -> scale 0, codes 0
     x[6, 1] = 0.0
     x[6, 1, 3] = -2.5                                    # single non-zero
-    x[7, 0] = np.linspace(-1, 1, D) * 1e-6               # tiny row: subnormal codes
+    x[7, 0] = np.linspace(-1, 1, D) * 1e-6               # tiny absmax: scale ~2e-9
     x[8, 1, :] = 1.0                                     # all equal to the max
     if src == "bf16":
         x = W.round_to_bf16(x)
@@ -153,3 +153,92 @@ def test_store_int8_bitexact(dev, D, src):
     if slots[7] >= 0:
         row = pool.k.cpu().numpy().reshape(nb * 16, hkv, D)[slots[7], 0, :8]
         assert row.tolist() == [127, 0, 2, 2, 0, -2, -2, 126]
+
+
+def _e4m3fn_edge_values(src):
+    """Values that pin an e4m3fn encoder, all within [-448, 448]: every non-negative
+    finite code value; every midpoint between adjacent codes (ties, including the
+    subnormal midpoints (2m+1) 2^-10 and the ones whose rounding carries into the next
+    exponent) and its two neighbours one unit in the last place of the source type away;
+    all of them with both signs, and -0. Midpoints have five significant bits, so they
+    are exact in fp32 and in bf16."""
+    from oracle import fp8 as ofp8
+    vals = ofp8.decode_table()[:0x7F]                  # 0, 2^-9 .. 448, increasing
+    mids = (vals[:-1] + vals[1:]) / 2
+    if src == "f32":
+        f = np.float32
+        dn = np.nextafter(mids.astype(f), f(-np.inf))
+        up = np.nextafter(mids.astype(f), f(np.inf))
+    else:   # one bf16 ulp: step the raw bits of the (exact) bf16 value
+        b = W.bf16_bits(mids.astype(np.float32)).astype(np.int32)
+        dn = ((b - 1).astype(np.uint32) << 16).view(np.float32)
+        up = ((b + 1).astype(np.uint32) << 16).view(np.float32)
+        dn[mids == 0] = 0.0
+    pos = np.concatenate([vals, mids, dn, up]).astype(np.float32)
+    pos = pos[(pos >= 0) & (pos <= 448)]
+    out = np.concatenate([pos, -pos, [np.float32(-0.0)]]).astype(np.float32)
+    if src == "bf16":
+        assert np.array_equal(W.round_to_bf16(out), out)
+    return out
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_store_fp8_encoder_edges_bitexact(dev, src):
+    """Rows whose absmax is exactly 448 have scale 448 / 448 = 1 exactly, so the kernel's
+    encoder sees the source values themselves: every code value, every midpoint between
+    adjacent codes (round half to even) and the neighbours of each midpoint, the
+    subnormal range, signed zeros, both signs. Extra rows whose absmax a gives
+    fl(a / fl(a / 448)) > 448 drive the encoder just past 448, where it must saturate to
+    0x7E / 0xFE (not produce the NaN code 0x7F). Codes and scales bit-exact against the
+    oracle quantiser."""
+    from oracle import fp8 as ofp8
+    D, hkv = 128, 1
+    vals = _e4m3fn_edge_values(src)
+    per = D - 1
+    nrows = -(-len(vals) // per)
+    x = np.zeros((nrows, hkv, D), np.float32)
+    for r in range(nrows):
+        chunk = vals[r * per:(r + 1) * per]
+        x[r, 0, 0] = 448.0 if r % 2 == 0 else -448.0     # absmax exactly 448
+        x[r, 0, 1:1 + len(chunk)] = chunk
+    # saturation rows: absmax values whose quantised image overshoots 448 by rounding
+    rng = np.random.default_rng(7)
+    a = rng.uniform(1, 1000, 4096).astype(np.float32)
+    if src == "bf16":
+        a = W.round_to_bf16(a)
+    y = (a / (a / np.float32(448)).astype(np.float32)).astype(np.float32)
+    over = a[y > 448][:6]
+    assert len(over) >= 4, "no overshooting absmax found"
+    sat = np.zeros((len(over), hkv, D), np.float32)
+    for i, av in enumerate(over):
+        sat[i, 0, :] = np.float32(av) * np.float32(0.25)
+        sat[i, 0, i % D] = av if i % 2 == 0 else -av
+    x = np.concatenate([x, sat]).astype(np.float32)
+    T = x.shape[0]
+    # the constructed rows hit what they are meant to hit (checked on the oracle side)
+    codes, scale = ofp8.quantize_rows(x)
+    assert np.all(scale[:nrows] == 1.0)
+    assert np.all(np.isin(codes[nrows:].reshape(len(over), -1).max(axis=1) & 0x7F, [0x7E]))
+    assert not np.any((codes & 0x7F) == 0x7F)
+    nb = -(-T // 16) + 1
+    slots = np.random.default_rng(8).permutation(nb * 16)[:T].astype(np.int64)
+    pool = pa.KVPool.empty(nb, hkv, D, "fp8", dev)
+    for t in (pool.k, pool.v):
+        t.fill_(0xAB)
+    for t in (pool.k_scale, pool.v_scale):
+        t.fill_(-7.0)
+    td = torch.bfloat16 if src == "bf16" else torch.float32
+    xk = torch.from_numpy(x).to(td).to(dev)
+    xv = torch.from_numpy(-x).to(td).to(dev)
+    pa.store_kv(pool, xk, xv, torch.from_numpy(slots).to(dev))
+    torch.cuda.synchronize()
+    c0 = np.full((nb, 16, hkv, D), 0xAB, np.uint8)
+    s0 = np.full((nb, 16, hkv), -7.0, np.float32)
+    ck, sk = ref.store_fp8_ref(c0, s0, x, slots)
+    cv, sv = ref.store_fp8_ref(c0, s0, -x, slots)
+    got_k = pool.k.cpu().numpy()
+    bad = np.argwhere(got_k != ck)
+    assert len(bad) == 0, f"{len(bad)} codes differ, first at {bad[:4].tolist()}"
+    assert np.array_equal(pool.k_scale.cpu().numpy().view(np.uint32), sk.view(np.uint32))
+    assert np.array_equal(pool.v.cpu().numpy(), cv)
+    assert np.array_equal(pool.v_scale.cpu().numpy().view(np.uint32), sv.view(np.uint32))
