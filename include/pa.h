@@ -35,7 +35,9 @@
  *    library never allocates, frees or caches device memory and keeps no global
  *    mutable state: all addressing is passed explicitly on every call, as [P1] "design
  *    decisions / explicit parameter passing" argues against a hidden current slot (the
- *    host block manager keeps its state in the handle the caller creates).
+ *    host block manager keeps its state in the handle the caller creates). The one
+ *    exception is pa_decode_noalloc's scratch array, a fixed block of device memory in
+ *    the library's code object (per GPU), for callers that cannot pass a workspace.
  *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
  *    default stream). They return after enqueueing and never synchronise.
  *  - Element strides are in ELEMENTS, not bytes; the innermost (head_dim) stride is
@@ -254,6 +256,32 @@ int pa_decode(void *out, int64_t out_stride_tok, int64_t out_stride_head, const 
               int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
               float scale, int32_t split_tokens, void *workspace, size_t workspace_bytes,
               void *stream);
+
+/*
+ * pa_decode_noalloc - pa_decode for callers that cannot allocate device memory (code
+ * under graph capture that must not allocate, tight serving loops, harnesses that
+ * forbid allocation): the same call without the workspace arguments.
+ *
+ * Its split partials and counters live in a scratch array of PA_NOALLOC_SCRATCH_BYTES
+ * that the library holds in device memory on every GPU it runs on, until the process
+ * ends (looked up, and its counters cleared by a small kernel on `stream`, on the first
+ * call on each device). The call allocates and frees nothing. Results are bit-identical
+ * to pa_decode with the same arguments and split length.
+ * Returns PA_ERR_WORKSPACE, launching nothing, when pa_decode_workspace_bytes(...) for
+ * this call exceeds PA_NOALLOC_SCRATCH_BYTES (use pa_decode with a workspace, or a
+ * longer split_tokens, then); other errors as pa_decode.
+ * Every call on one GPU shares that GPU's array: calls that can overlap on one GPU
+ * (different streams, or a graph replay beside an eager call) race and must not be
+ * made; calls on one stream are ordered and safe.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int pa_decode_noalloc(void *out, int64_t out_stride_tok, int64_t out_stride_head,
+                      const void *q, int64_t q_stride_tok, int64_t q_stride_head,
+                      int32_t q_dtype, int32_t num_seqs, int32_t q_heads,
+                      const pa_kv_pool_t *pool, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *context_lens,
+                      int32_t max_context_len, float scale, int32_t split_tokens,
+                      void *stream);
 
 /*
  * pa_decode_step - one decode step of a layer: store each sequence's new K/V row, then

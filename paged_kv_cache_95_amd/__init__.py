@@ -23,6 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
 PA_OK = 0
 BLOCK_SIZE = 16
+# bytes of the per-GPU scratch array behind decode_noalloc (PA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _DTYPE_CODE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
                torch.int8: PA_INT8}
@@ -77,6 +79,9 @@ SIGNATURES = {
     "pa_decode_step": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32,
                                       ctypes.POINTER(_Pool), _P, _P, _I32, _I64, _I64, _I64,
                                       _I64, _P, _P, _I32, _P, _I32, _F, _I32, _P, _SZ, _P]),
+    "pa_decode_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _I32, _I32,
+                                         ctypes.POINTER(_Pool), _P, _I32, _P, _I32, _F, _I32,
+                                         _P]),
     "pa_varlen_prefill_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
     "pa_varlen_prefill": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _I32, _P, _I32, _I64,
                                          _I32, _I32, ctypes.POINTER(_Pool), _P, _I32, _P, _I32,
@@ -368,6 +373,32 @@ def decode(q, pool, block_tables, context_lens, scale, max_context_len=None, spl
                            _ptr(context_lens), int(max_context_len), float(scale),
                            int(split_tokens), _ptr(workspace), wbytes, _stream()),
            "pa_decode")
+    return out
+
+
+def decode_noalloc(q, pool, block_tables, context_lens, scale, max_context_len=None,
+                   split_tokens=0, out=None):
+    """decode() without a workspace: the library's per-GPU scratch array holds the split
+    partials, so the call allocates nothing on the device (pass `out` to keep this
+    function from allocating it). Calls that could overlap on one GPU must not be made.
+    Raises PaError (PA_ERR_WORKSPACE) when the call needs more than
+    NOALLOC_SCRATCH_BYTES of workspace."""
+    qs = _rows3(q, "q")
+    B, Hq, D = q.shape
+    _meta(block_tables, context_lens, B)
+    if max_context_len is None:
+        max_context_len = block_tables.shape[1] * pool.block_size
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    os_ = _rows3(out, "out")
+    _rows_like(q, out, pool)
+    _one_device(q, out, block_tables, context_lens, pool.k)
+    _check(lib().pa_decode_noalloc(_ptr(out), os_[0], os_[1], _ptr(q), qs[0], qs[1],
+                                   _DTYPE_CODE[q.dtype], B, Hq, pool.struct, _ptr(block_tables),
+                                   block_tables.shape[1], _ptr(context_lens),
+                                   int(max_context_len), float(scale), int(split_tokens),
+                                   _stream()),
+           "pa_decode_noalloc")
     return out
 
 

@@ -265,6 +265,33 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
   return launched(pa::launch_decode(*pool, a, (hipStream_t)stream));
 }
 
+int pa_decode_noalloc(void* out, int64_t out_stride_tok, int64_t out_stride_head,
+                      const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                      int32_t q_dtype, int32_t num_seqs, int32_t q_heads,
+                      const pa_kv_pool_t* pool, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, float scale, int32_t split_tokens,
+                      void* stream) {
+  pa::DecodeArgs a;
+  bool nothing = false;
+  // validated against the scratch array's size; its device address is looked up only
+  // for a call that launches (a placeholder stands in for it until then)
+  void* const placeholder = reinterpret_cast<void*>(uintptr_t{256});
+  const int st = prepare_decode(out, out_stride_tok, out_stride_head, q, q_stride_tok,
+                                q_stride_head, q_dtype, num_seqs, q_heads, pool, block_tables,
+                                max_blocks_per_seq, context_lens, max_context_len, scale,
+                                split_tokens, placeholder, pa::kNoallocScratchBytes, &a,
+                                &nothing);
+  if (st != PA_OK || nothing) return st;
+  if (a.counters != nullptr) {
+    void* scratch = nullptr;
+    const int s2 = pa::noalloc_scratch(&scratch, (hipStream_t)stream);
+    if (s2 != PA_OK) return s2;
+    bind_decode_workspace(&a, scratch);
+  }
+  return launched(pa::launch_decode(*pool, a, (hipStream_t)stream));
+}
+
 int pa_decode_step(void* out, int64_t out_stride_tok, int64_t out_stride_head, const void* q,
                    int64_t q_stride_tok, int64_t q_stride_head, int32_t q_dtype,
                    int32_t num_seqs, int32_t q_heads, const pa_kv_pool_t* pool,

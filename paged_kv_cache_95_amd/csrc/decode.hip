@@ -34,6 +34,7 @@
 // (the tail of the last block) are excluded by selects, never by multiplying with
 // zero, so stale or NaN slots cannot leak in.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
@@ -1430,6 +1431,44 @@ static int dispatch(const pa_kv_pool_t& pool, const DecodeArgs& a, const StepRow
 
 int launch_decode(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream) {
   return dispatch(pool, a, nullptr, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free decode
+// The workspace of pa_decode_noalloc: one array per GPU, in the library's code object,
+// held until the process ends. Host code never uses the array's name as an address
+// (on the host it names a stand-in, not device memory): its device address is looked
+// up once per device with hipGetSymbolAddress and that pointer is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+__global__ void zero_words_kernel(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxScratchDevices = 64;
+
+int noalloc_scratch(void** ptr, hipStream_t stream) {
+  static std::mutex mu;
+  static void* dev_ptr[kMaxScratchDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    // with `dev` current: this device's copy of the array
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PA_ERR_HIP;
+    // the arrival / work counters at the start of a decode workspace must be zero before
+    // its first use (every call leaves them zero again); a kernel, not a memset, so that
+    // a first call under graph capture records an ordinary kernel node
+    constexpr int words = (int)(kDecodeCounterBytes / sizeof(unsigned));
+    zero_words_kernel<<<(words + 255) / 256, 256, 0, stream>>>((unsigned*)p, words);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return PA_OK;
 }
 
 int launch_decode_step(const pa_kv_pool_t& pool, const DecodeArgs& a, const StepRows& rows,

@@ -59,6 +59,13 @@ constexpr size_t kDecodeCounterBytes = kDecodeCounters * sizeof(unsigned);
 
 int launch_decode(const pa_kv_pool_t& pool, const DecodeArgs& a, hipStream_t stream);
 
+// Size of pa_decode_noalloc's per-device scratch array (the same value as
+// PA_NOALLOC_SCRATCH_BYTES in pa.h).
+constexpr size_t kNoallocScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+// Device address of the current device's scratch array (looked up, and its counter
+// block cleared by a kernel on `stream`, on the first call on that device).
+int noalloc_scratch(void** ptr, hipStream_t stream);
+
 // New rows of a decode step: row s of k / v ([num_seqs, kv_heads, head_dim] of src_dtype,
 // element strides) is sequence s's newest token, to be stored at slots[s] (< 0: none).
 struct StepRows {

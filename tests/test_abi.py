@@ -107,6 +107,27 @@ def test_decode_validation(lib):
     assert decode(lib, p, split=16, ws=0xC008, wsb=need) == WORKSPACE    # not 16-B aligned
 
 
+def noalloc(lib, pool, B=2, Hq=12, maxb=8, maxctx=128, split=16, out=0x8000):
+    return lib.pa_decode_noalloc(out, 1536, 128, 0x9000, 1536, 128, pa.PA_BF16, B, Hq,
+                                 ctypes.byref(pool), 0xA000, maxb, 0xB000, maxctx, 0.1, split,
+                                 None)
+
+
+def test_decode_noalloc_validation(lib):
+    """Rejected on the host before the scratch array is looked up or anything launched:
+    the argument errors of pa_decode, and calls needing more than the array holds."""
+    p = fake_pool()
+    assert noalloc(lib, p, B=0) == OK
+    assert noalloc(lib, p, Hq=13) == INVALID
+    assert noalloc(lib, p, Hq=18) == UNSUPPORTED
+    assert noalloc(lib, p, out=0) == INVALID
+    assert noalloc(lib, p, split=8) == INVALID
+    # 256 sequences x 16 heads x 2048 splits of 16 tokens: far beyond 64 MiB of partials
+    need = lib.pa_decode_workspace_bytes(256, 16, 2, 128, 32768, 16)
+    assert need > pa.NOALLOC_SCRATCH_BYTES
+    assert noalloc(lib, p, B=256, Hq=16, maxb=2048, maxctx=32768, split=16) == WORKSPACE
+
+
 def step(lib, pool, src=pa.PA_BF16, B=2, k=0xC000, v=0xD000, sm=0xE000, kst=256, ws=0, wsb=0):
     return lib.pa_decode_step(0x8000, 1536, 128, 0x9000, 1536, 128, pa.PA_BF16, B, 12,
                               ctypes.byref(pool), k, v, src, kst, 128, kst, 128, sm, 0xA000, 8,
