@@ -67,9 +67,11 @@ def test_eviction_is_least_recently_released_and_tail_first():
     assert r.table(3) == ([0, 1, 2], 5)
 
 
-def _random_ops(seed, nblocks, bs, steps, prefix_caching):
+def _random_ops(seed, nblocks, bs, steps, prefix_caching, make=pa.BlockManager):
+    """Random add / append / fork / free operations on the library's manager (made by
+    `make`) and on the reference model, compared after every operation."""
     rng = np.random.default_rng(seed)
-    lib = pa.BlockManager(nblocks, bs, prefix_caching)
+    lib = make(nblocks, bs, prefix_caching)
     ref = BlockManagerRef(nblocks, bs, prefix_caching)
     live, next_id = [], 0
     prompts = [list(rng.integers(0, 50, 40)) for _ in range(4)]   # shared prefixes
