@@ -61,6 +61,7 @@
  *    range, 1 <= context_lens[s] <= max_context_len, n_s <= context_lens[s]) are the
  *    caller's contract; the kernels skip out-of-range block ids and slots rather than
  *    touch memory outside the pool, and the affected outputs are then unspecified.
+ *    The PA_DEBUG_CHECKS build reports such violations (pa_debug_take_violation).
  *  - Concurrent calls on different streams are safe when their outputs (and
  *    workspaces) are disjoint.
  */
@@ -88,7 +89,9 @@ enum {
   PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad stride, bad dtype combo */
   PA_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, block_size, group size */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_bytes() */
-  PA_ERR_HIP = -4          /* a kernel launch failed */
+  PA_ERR_HIP = -4,         /* a kernel launch failed */
+  PA_ERR_DEVICE_DATA = -5  /* PA_DEBUG_CHECKS build only: an earlier call's device-side
+                              metadata broke its contract (pa_debug_take_violation) */
 };
 
 /* One layer's KV pool. Caller-owned, dense, persists across calls (it is the cache).
@@ -110,6 +113,41 @@ typedef struct pa_kv_pool {
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *pa_status_string(int status);
+
+/*
+ * Debug build (libpa_debug.so, compiled with PA_DEBUG_CHECKS). The device-side
+ * preconditions of the calls below are the caller's contract, and the release kernels
+ * only make sure a broken one cannot take them outside their buffers (out-of-range
+ * block ids and slots are skipped, lengths clamped; the affected outputs are then
+ * unspecified) - the wrong-slot and context-length bugs [P4] "errors encountered"
+ * types 1, 2 and 5 describe would pass silently. In the debug build every kernel call
+ * first launches a check of the metadata it is about to use, on the same stream; the
+ * first violation is recorded in a per-GPU word, and the call then runs as in the
+ * release build (nothing faults). Every later call waits for its stream, reads the
+ * word and, while a violation is recorded, returns PA_ERR_DEVICE_DATA and launches
+ * nothing; pa_debug_take_violation reads and clears it. Debug calls synchronise and
+ * cannot be captured in a graph.
+ * Violations (code, and what `where` holds):
+ */
+enum {
+  PA_VIOLATION_CONTEXT_LEN = 1, /* context_lens[s] outside [1, max_context_len] (decode) or
+                                   [0, max_context_len] (varlen); where = s */
+  PA_VIOLATION_BLOCK_ID = 2,    /* block_tables[s][j] outside [0, num_blocks) for a block the
+                                   context uses (j < ceil(L/16)); where = s << 28 | j */
+  PA_VIOLATION_SLOT = 3,        /* slot_mapping[t] >= num_blocks * block_size; where = t */
+  PA_VIOLATION_CHUNK = 4,       /* varlen chunk longer than its context: n_s > L_s; where = s */
+  PA_VIOLATION_CU_SEQLENS = 5,  /* cu_seqlens not 0 .. total_tokens non-decreasing, or a
+                                   chunk longer than max_q_len; where = s */
+  PA_VIOLATION_STEP_SLOT = 6,   /* pa_decode_step: slot_mapping[s] >= 0 but not the slot of
+                                   position context_lens[s] - 1; where = s */
+  PA_VIOLATION_POSITION = 7     /* pa_rope_store_kv: positions[t] outside [0, max_position);
+                                   where = t */
+};
+/* 1 in the PA_DEBUG_CHECKS build, 0 in the release build. */
+int32_t pa_debug_checks(void);
+/* Waits for `stream`, then returns (and clears) the current GPU's recorded violation:
+ * *code = 0 when there is none. Never fails with PA_ERR_DEVICE_DATA itself. */
+int pa_debug_take_violation(void *stream, int32_t *code, int64_t *where);
 
 /*
  * pa_store_kv - scatter new K/V rows into the pool through slot_mapping.

@@ -19,10 +19,16 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
+# the same library built with PA_DEBUG_CHECKS (device-data contract checks; see pa.h)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libpa_debug.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3
 PA_OK = 0
+PA_ERR_DEVICE_DATA = -5
 BLOCK_SIZE = 16
+# contract violations a PA_DEBUG_CHECKS build records (pa.h)
+VIOLATIONS = {1: "context_len", 2: "block_id", 3: "slot", 4: "chunk", 5: "cu_seqlens",
+              6: "step_slot", 7: "position"}
 # bytes of the per-GPU scratch array behind decode_noalloc (PA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -54,6 +60,8 @@ _lib = None
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_debug_checks": (_I32, []),
+    "pa_debug_take_violation": (ctypes.c_int, [_P, _P, _P]),
     "pa_decode_default_split_tokens": (_I32, [_I32, _I32, _I32]),
     "pa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_store_kv": (ctypes.c_int, [ctypes.POINTER(_Pool), _P, _P, _I32, _I64, _I64, _I64, _I64,
@@ -89,20 +97,53 @@ SIGNATURES = {
 }
 
 
+def _load(path):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m paged_kv_cache_95_amd.build`")
+    l = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(l, name)
+        fn.restype = res
+        fn.argtypes = args
+    return l
+
+
 def lib():
     """Load libpa.so (once). Raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m paged_kv_cache_95_amd.build`")
-        l = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(l, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = l
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def use_library(path):
+    """Make every call of this module go through the library at `path` (e.g.
+    DEBUG_LIB_PATH) from now on; returns the one used so far, to restore it with
+    use_library_handle()."""
+    global _lib
+    prev = lib()
+    _lib = _load(path)
+    return prev
+
+
+def use_library_handle(handle):
+    global _lib
+    _lib = handle
+
+
+def debug_checks():
+    """True when the loaded library is the PA_DEBUG_CHECKS build."""
+    return bool(lib().pa_debug_checks())
+
+
+def take_violation():
+    """Wait for the current stream, then return and clear the GPU's recorded contract
+    violation as (name, code, where); (None, 0, 0) when there is none."""
+    code, where = ctypes.c_int32(0), ctypes.c_int64(0)
+    _check(lib().pa_debug_take_violation(_stream(), ctypes.byref(code), ctypes.byref(where)),
+           "pa_debug_take_violation")
+    return VIOLATIONS.get(code.value), int(code.value), int(where.value)
 
 
 def status_string(status):

@@ -3,7 +3,10 @@
     python -m paged_kv_cache_95_amd.build [--jobs N]
 
 Compiles every source under csrc/ to an object file in parallel, then links
-paged_kv_cache_95_amd/libpa.so. Always recompiles (this is the build check).
+paged_kv_cache_95_amd/libpa.so and the debug build paged_kv_cache_95_amd/libpa_debug.so
+(the same objects, with the C ABI layer compiled with PA_DEBUG_CHECKS: device-data
+contract checks ahead of every kernel call). Always recompiles (this is the build
+check).
 """
 import argparse
 import concurrent.futures as cf
@@ -15,6 +18,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libpa.so")
+OUT_DEBUG = os.path.join(HERE, "libpa_debug.so")
+# the source compiled a second time, with -DPA_DEBUG_CHECKS, for libpa_debug.so
+DEBUG_LAYER = "api.cpp"
 BUILD_DIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
@@ -37,30 +43,43 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def compile_one(src):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def compile_one(src, debug=False):
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + (".debug.o" if debug else ".o"))
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + lang + COMMON + ["-c", src, "-o", obj]
+    flags = ["-DPA_DEBUG_CHECKS=1"] if debug else []
+    cmd = [hipcc()] + lang + COMMON + flags + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs=None, verbose=True):
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), os.cpu_count() or 4)
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(compile_one, srcs))
-    tmp = OUT + ".tmp"
+def link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(jobs=None, verbose=True):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    debug_src = [f for f in srcs if os.path.basename(f) == DEBUG_LAYER]
+    jobs = jobs or min(len(srcs) + 1, os.cpu_count() or 4)
+    # the slowest sources first, so that the pool is not left waiting on one of them
+    order = sorted(srcs, key=lambda f: -os.path.getsize(f))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        futs = {f: ex.submit(compile_one, f) for f in order}
+        dbg = [ex.submit(compile_one, f, True) for f in debug_src]
+        objs = [futs[f].result() for f in srcs]
+        dbg_objs = [d.result() for d in dbg]
+    link(objs, OUT)
+    debug_of = dict(zip(debug_src, dbg_objs))
+    link([debug_of.get(f, o) for f, o in zip(srcs, objs)], OUT_DEBUG)
     if verbose:
-        print(f"built {OUT}", flush=True)
+        print(f"built {OUT} and {OUT_DEBUG}", flush=True)
     return OUT
 
 

@@ -65,6 +65,31 @@ int launched(int status) {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+// PA_DEBUG_CHECKS build: before a call launches, wait for its stream and refuse it while
+// an earlier call's violation is recorded, then launch the check of this call's device
+// metadata ahead of its kernels. The release build compiles these to nothing.
+#ifdef PA_DEBUG_CHECKS
+constexpr int kDebugBuild = 1;
+#define PA_DEBUG_GATE(stream)                                           \
+  do {                                                                  \
+    const int gate_ = pa::debug_gate((hipStream_t)(stream));            \
+    if (gate_ != PA_OK) return gate_;                                   \
+  } while (0)
+#define PA_DEBUG_CHECK(call)                                            \
+  do {                                                                  \
+    const int check_ = (call);                                          \
+    if (check_ != PA_OK) return check_;                                 \
+  } while (0)
+#else
+constexpr int kDebugBuild = 0;
+#define PA_DEBUG_GATE(stream) \
+  do {                        \
+  } while (0)
+#define PA_DEBUG_CHECK(call) \
+  do {                       \
+  } while (0)
+#endif
+
 }  // namespace
 
 extern "C" {
@@ -76,6 +101,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape or dtype not supported";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
+    case PA_ERR_DEVICE_DATA:
+      return "PA_ERR_DEVICE_DATA: an earlier call's device metadata broke its contract "
+             "(pa_debug_take_violation)";
     default: return "unknown pa status";
   }
 }
@@ -84,6 +112,13 @@ int32_t pa_decode_default_split_tokens(int32_t num_seqs, int32_t kv_heads,
                                        int32_t max_context_len) {
   if (num_seqs <= 0 || kv_heads <= 0 || max_context_len <= 0) return 0;
   return effective_split(0, num_seqs, kv_heads, max_context_len);
+}
+
+int32_t pa_debug_checks(void) { return kDebugBuild; }
+
+int pa_debug_take_violation(void* stream, int32_t* code, int64_t* where) {
+  if (!code || !where) return PA_ERR_INVALID_ARG;
+  return pa::debug_take((hipStream_t)stream, code, where);
 }
 
 
@@ -134,6 +169,9 @@ int pa_rope_store_kv(const pa_kv_pool_t* pool, const void* q, int64_t q_stride_t
   a.sin_table = sin_table;
   a.max_position = max_position;
   a.slots = slot_mapping;
+  PA_DEBUG_GATE(stream);
+  PA_DEBUG_CHECK(pa::validate_tokens(*pool, slot_mapping, num_tokens, positions, max_position,
+                                     (hipStream_t)stream));
   return launched(pa::launch_rope_store(*pool, a, src_dtype, (hipStream_t)stream));
 }
 
@@ -144,6 +182,7 @@ int pa_copy_blocks(const pa_kv_pool_t* pool, const int32_t* src_blocks,
   if (num_pairs < 0) return PA_ERR_INVALID_ARG;
   if (num_pairs == 0) return PA_OK;
   if (!src_blocks || !dst_blocks) return PA_ERR_INVALID_ARG;
+  PA_DEBUG_GATE(stream);
   return launched(pa::launch_copy_blocks(*pool, src_blocks, dst_blocks, num_pairs,
                                          (hipStream_t)stream));
 }
@@ -172,6 +211,9 @@ int pa_store_kv(const pa_kv_pool_t* pool, const void* k, const void* v, int32_t 
                             v_stride_head);
   if (status != PA_OK || num_tokens == 0) return status;
   if (!k || !v || !slot_mapping) return PA_ERR_INVALID_ARG;
+  PA_DEBUG_GATE(stream);
+  PA_DEBUG_CHECK(pa::validate_tokens(*pool, slot_mapping, num_tokens, nullptr, 0,
+                                     (hipStream_t)stream));
   return launched(pa::launch_store(*pool, k, v, src_dtype, num_tokens, k_stride_tok,
                                    k_stride_head, v_stride_tok, v_stride_head, slot_mapping,
                                    (hipStream_t)stream));
@@ -262,6 +304,9 @@ int pa_decode(void* out, int64_t out_stride_tok, int64_t out_stride_head, const 
                                 max_blocks_per_seq, context_lens, max_context_len, scale,
                                 split_tokens, workspace, workspace_bytes, &a, &nothing);
   if (st != PA_OK || nothing) return st;
+  PA_DEBUG_GATE(stream);
+  PA_DEBUG_CHECK(pa::validate_decode(*pool, block_tables, max_blocks_per_seq, context_lens,
+                                     num_seqs, max_context_len, nullptr, (hipStream_t)stream));
   return launched(pa::launch_decode(*pool, a, (hipStream_t)stream));
 }
 
@@ -283,6 +328,9 @@ int pa_decode_noalloc(void* out, int64_t out_stride_tok, int64_t out_stride_head
                                 split_tokens, placeholder, pa::kNoallocScratchBytes, &a,
                                 &nothing);
   if (st != PA_OK || nothing) return st;
+  PA_DEBUG_GATE(stream);
+  PA_DEBUG_CHECK(pa::validate_decode(*pool, block_tables, max_blocks_per_seq, context_lens,
+                                     num_seqs, max_context_len, nullptr, (hipStream_t)stream));
   if (a.counters != nullptr) {
     void* scratch = nullptr;
     const int s2 = pa::noalloc_scratch(&scratch, (hipStream_t)stream);
@@ -322,6 +370,10 @@ int pa_decode_step(void* out, int64_t out_stride_tok, int64_t out_stride_head, c
   rows.v_st = v_stride_tok;
   rows.v_sh = v_stride_head;
   rows.slots = slot_mapping;
+  PA_DEBUG_GATE(stream);
+  PA_DEBUG_CHECK(pa::validate_decode(*pool, block_tables, max_blocks_per_seq, context_lens,
+                                     num_seqs, max_context_len, slot_mapping,
+                                     (hipStream_t)stream));
   return launched(pa::launch_decode_step(*pool, a, rows, (hipStream_t)stream));
 }
 
@@ -405,6 +457,8 @@ int pa_varlen_prefill(void* out, int64_t out_stride_tok, int64_t out_stride_head
   a.ws_lse = max_chunks > 1
                  ? a.ws_o + (size_t)total_tokens * q_heads * max_chunks * pool->head_dim
                  : nullptr;
+  PA_DEBUG_GATE(stream);
+  PA_DEBUG_CHECK(pa::validate_varlen(*pool, a, (hipStream_t)stream));
   return launched(pa::launch_prefill(*pool, a, (hipStream_t)stream));
 }
 

@@ -144,4 +144,18 @@ inline int64_t prefill_plan_bound(int64_t total_tokens, int64_t q_heads, int64_t
 
 int launch_prefill(const pa_kv_pool_t& pool, const PrefillArgs& a, hipStream_t stream);
 
+// Device-data checks (launched by the PA_DEBUG_CHECKS build of api.cpp only; the
+// release build never calls them). Each records the first contract violation it sees
+// in the current GPU's violation word.
+int validate_decode(const pa_kv_pool_t& pool, const int32_t* block_tables, int max_blocks,
+                    const int32_t* ctx, int num_seqs, int max_ctx, const int64_t* slots,
+                    hipStream_t stream);
+int validate_tokens(const pa_kv_pool_t& pool, const int64_t* slots, int64_t n,
+                    const int64_t* positions, int64_t max_position, hipStream_t stream);
+int validate_varlen(const pa_kv_pool_t& pool, const PrefillArgs& a, hipStream_t stream);
+// Waits for `stream` and reads the violation word: PA_ERR_DEVICE_DATA while one is set.
+int debug_gate(hipStream_t stream);
+// Waits for `stream`, returns the recorded violation (code 0: none) and clears it.
+int debug_take(hipStream_t stream, int32_t* code, int64_t* where);
+
 }  // namespace pa

@@ -28,6 +28,15 @@ int launch_rope_store(const pa_kv_pool_t&, const RopeArgs&, int, hipStream_t) {
 }
 int launch_prefill(const pa_kv_pool_t&, const PrefillArgs&, hipStream_t) { reached("launch_prefill"); }
 int noalloc_scratch(void**, hipStream_t) { reached("noalloc_scratch"); }
+int validate_decode(const pa_kv_pool_t&, const int32_t*, int, const int32_t*, int, int,
+                    const int64_t*, hipStream_t) { reached("validate_decode"); }
+int validate_tokens(const pa_kv_pool_t&, const int64_t*, int64_t, const int64_t*, int64_t,
+                    hipStream_t) { reached("validate_tokens"); }
+int validate_varlen(const pa_kv_pool_t&, const PrefillArgs&, hipStream_t) {
+  reached("validate_varlen");
+}
+int debug_gate(hipStream_t) { reached("debug_gate"); }
+int debug_take(hipStream_t, int32_t*, int64_t*) { reached("debug_take"); }
 }  // namespace pa
 
 extern "C" hipError_t hipGetLastError(void) { reached("hipGetLastError"); }
