@@ -141,6 +141,22 @@ def capture(torch, fn):
     return g
 
 
+SETTLE_S = 0.25
+
+
+def settle(torch, graph, seconds=None):
+    """Replay until `seconds` of GPU work have run, so that the timed replays see the
+    GPU's steady clocks rather than its ramp from idle (short timed windows right after
+    setup read several percent slow otherwise)."""
+    seconds = SETTLE_S if seconds is None else seconds
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            graph.replay()
+        torch.cuda.synchronize()
+
+
 # ----------------------------------------------------------------------------- headline
 
 def large_decode(torch, pa, W, dev, steps, warmup):
@@ -167,6 +183,7 @@ def large_decode(torch, pa, W, dev, steps, warmup):
         pa.decode(q, pool, bt, ctx, case.scale, max_context_len=maxctx, out=out, workspace=ws)
 
     g_step, g_dec = capture(torch, step), capture(torch, dec)
+    settle(torch, g_step)
     for _ in range(warmup):
         g_step.replay()
     torch.cuda.synchronize()
@@ -227,8 +244,7 @@ def qwen_step(torch, pa, W, dev, reps):
                       workspace=ws)
 
     g, g2 = capture(torch, step), capture(torch, two_calls)
-    for _ in range(3):
-        g.replay()
+    settle(torch, g)
     ms = time_graph(torch, g, reps)
     ms2 = time_graph(torch, g2, reps)
     dby = decode_bytes(case.context_lens, hq, hkv, D, 2)
@@ -286,8 +302,7 @@ def quant_decode(torch, pa, W, dev, reps, dtype, copies=2):
             pa.store_kv(p, kn, vn, slots)
 
     g, gs = capture(torch, dec), capture(torch, sto)
-    for _ in range(3):
-        g.replay()
+    settle(torch, g)
     ms = time_graph(torch, g, reps) / copies
     ms_store = time_graph(torch, gs, reps) / copies
     by = decode_bytes(case.context_lens, case.Hq, hkv, D, 1, scales=True)
@@ -329,6 +344,7 @@ def varlen_prefill(torch, pa, W, dev, reps):
 
     g = capture(torch, run)
     gs = capture(torch, lambda: pa.store_kv(pool, kn, vn, slots))
+    settle(torch, g)
     ms = time_graph(torch, g, reps)
     ms_store = time_graph(torch, gs, reps)
     fl = prefill_flops(case.extra["n"], case.extra["P"], case.Hq, case.D)
@@ -357,6 +373,7 @@ def copy_probe(torch, dev, reps=20):
     a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
     b = torch.empty_like(a)
     g = capture(torch, lambda: b.copy_(a))
+    settle(torch, g)
     ms = time_graph(torch, g, reps)
     by = 2 * a.numel() * a.element_size()
     del a, b
@@ -438,6 +455,7 @@ def cpu_baseline(nsample=256, max_workers=16):
 # ----------------------------------------------------------------------------- main
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
@@ -446,7 +464,10 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", choices=WORKLOADS, default=None,
                     help="run one workload (for profiling); prints its figures only")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed replays before each timing (steady clocks)")
     args = ap.parse_args()
+    SETTLE_S = args.settle
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs on a "
               "single GPU; the path shards by sequence or KV head with no exchange, so one "
