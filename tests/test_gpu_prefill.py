@@ -149,3 +149,22 @@ def test_chunked_prefill_equals_one_shot(dev):
     assert max_err(o1, exp[rows1]) <= TOL["bf16"]
     assert max_err(o2, exp[rows2]) <= TOL["bf16"]
     assert torch.max(torch.abs(o1.float() - whole[r1].float())).item() <= 2 * TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,split", [(1100, 64), (300, 64)])
+def test_many_sequences_split_tiles_workspace_reused(dev, B, split):
+    """Hundreds to over a thousand short chunks (the work list's sequence cache holds
+    4096, the plan launch 1024 threads), many of their row tiles split into 64-key
+    chunks; two calls in a row on one workspace give the same result."""
+    case = W.random_case(27 + B, kind="varlen", B=B, Hq=8, Hkv=2, D=64, lmin=1, lmax=160,
+                         nmax=24)
+    s = Setup(case, dev)
+    T = s.q.shape[0]
+    ws = pa.varlen_prefill_workspace(T, 8, 64, case.max_context_len, split, device=dev)
+    exp = s.oracle()
+    for rep in range(2):
+        out = s.gpu(split_tokens=split, workspace=ws)
+        torch.cuda.synchronize()
+        err = max_err(out, exp)
+        print(f"B={B} split={split} rep={rep} max_abs_err={err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
