@@ -215,7 +215,8 @@ struct SplitArgs {
   int max_splits;
   float* ws_o;       // [num_seqs, q_heads, max_splits, D] split (or group) partials
   float* ws_lse;     // [num_seqs, q_heads, max_splits]
-  int max_chunks;    // ceil(max_splits / kGroupSplits): groups per sequence, at most
+  int group_splits;  // splits per level-1 merge group (GroupSplits<pool dtype>)
+  int max_chunks;    // ceil(max_splits / group_splits): groups per sequence, at most
   unsigned* counters;  // [num_seqs, kv_heads] arrival counters, zero between calls
   // Decode step with the store folded in (single-launch schedule only; knew == nullptr
   // otherwise): row s of knew / vnew ([num_seqs, kv_heads, D] of the pool dtype, element
@@ -865,18 +866,31 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(SplitArgs a) 
 // padding the grid to max_context_len would launch mostly empty workgroups.
 constexpr int kMaxCompactSeqs = 4096;
 
-// Partials are merged in groups of this many consecutive splits (see the merge below).
-constexpr int kGroupSplits = 8;
-// Calls with at most this many (sequence, group, KV head) workgroups take the single-
-// launch schedule; larger ones the persistent split kernel plus a merge launch.
+// The single-launch schedule's workgroup: eight waves, in one unit or two. Quantised
+// pools (128-byte head rows at two KV heads: half of each token's 256-byte record)
+// take two units of four waves, so that both halves of a record are read by one CU at
+// about the same time; other pools one unit of eight.
+constexpr int kFusedWaves = 8;
+template <int KVT>
+struct FusedUnits {
+  static constexpr int value = kQuant<KVT> ? 2 : 1;
+};
+// Partials are merged in groups of this many consecutive splits (a unit's waves; see
+// the merge below), in both schedules alike.
+template <int KVT>
+struct GroupSplits {
+  static constexpr int value = kFusedWaves / FusedUnits<KVT>::value;
+};
+constexpr int kMaxGroupSplits = kFusedWaves;
+// Calls with at most this many single-launch workgroups take that schedule; larger
+// ones the persistent split kernel plus a merge launch.
 constexpr int64_t kFusedMaxWorkgroups = 1024;
 // Words of the workspace's counter block: the single-launch schedule uses one per
-// (sequence, KV head) and only when a sequence has two or more groups, so at most
-// kFusedMaxWorkgroups / 2 of them; the persistent schedule's work counter and
-// leaver count use the last two.
+// (sequence, KV head) when a sequence has two or more groups (the launch checks that
+// they stay below the next two); the persistent schedule's work counter and leaver
+// count use the last two.
 constexpr int kCompactQueueWord = kDecodeCounters - 2;
 constexpr int kCompactDoneWord = kDecodeCounters - 1;
-static_assert(kFusedMaxWorkgroups / 2 <= kCompactQueueWord, "counter words overlap");
 
 __device__ __forceinline__ int block_exclusive_scan(int x, int* wave_sums, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -975,7 +989,8 @@ __global__ void __launch_bounds__(64 * kWaves, (MmaPath<KVT, G>::value) ? 2 : 1)
 
 // ---------------------------------------------------------------- log-sum-exp merge
 // Partials are merged in two levels, in index order: the splits of each group of
-// kGroupSplits consecutive splits first, then the groups. Both schedules below follow
+// group_splits consecutive splits first (GroupSplits<pool dtype>: 4 for quantised
+// pools, else 8), then the groups. Both schedules below follow
 // exactly this order with the same float operations, so a sequence's output bits
 // depend only on its own length and split_tokens, whichever schedule runs.
 //   level 1 (group c):  M = max lse_i, den = sum 2^(lse_i - M), acc = sum 2^(lse_i - M) o_i
@@ -1119,17 +1134,18 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(SplitArgs a
   const int h = t / D4, d = 4 * (t % D4);
   const int qh = g * G + h;
   const int64_t row0 = ((int64_t)s * a.hkv * G + qh) * a.max_splits;
-  const int ngroups = (nsplit + kGroupSplits - 1) / kGroupSplits;
+  const int gs = a.group_splits;
+  const int ngroups = (nsplit + gs - 1) / gs;
   Merge4 top;
   top.init();
   for (int c = 0; c < ngroups; ++c) {
-    // level 1 over the (at most kGroupSplits) splits of group c
-    const int i0 = c * kGroupSplits;
-    const int n = min(kGroupSplits, nsplit - i0);
-    float lse[kGroupSplits];
-    float4 o[kGroupSplits];
+    // level 1 over the (at most group_splits) splits of group c
+    const int i0 = c * gs;
+    const int n = min(gs, nsplit - i0);
+    float lse[kMaxGroupSplits];
+    float4 o[kMaxGroupSplits];
 #pragma unroll
-    for (int u = 0; u < kGroupSplits; ++u) {
+    for (int u = 0; u < kMaxGroupSplits; ++u) {
       const int64_t row = row0 + i0 + (u < n ? u : 0);
       lse[u] = u < n ? a.ws_lse[row] : -__builtin_huge_valf();
       o[u] = *reinterpret_cast<const float4*>(a.ws_o + row * D + d);
@@ -1137,7 +1153,7 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(SplitArgs a
     Merge4 grp;
     grp.init();
 #pragma unroll
-    for (int u = 0; u < kGroupSplits; ++u) grp.add(lse[u], o[u]);
+    for (int u = 0; u < kMaxGroupSplits; ++u) grp.add(lse[u], o[u]);  // -inf past n: no-op
     if (ngroups == 1) {
       store_out4<QT>(a.out, a.out_st, a.out_sh, a.out_aligned, s, qh, d, grp.acc, 1.0f / grp.den);
       return;
@@ -1152,25 +1168,35 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(SplitArgs a
 }
 
 // Single-launch schedule for small batches (latency bound: a handful of sequences
-// whose whole KV fits in one pass of the GPU). One workgroup of kGroupSplits waves per
-// (sequence, group of kGroupSplits consecutive splits, KV head), on a plain grid: the
-// item's query rows and block ids are requested before its context length is known,
-// the waves' partials are merged in LDS (level 1), and a sequence with several groups
-// publishes group partials to the workspace and counts arrivals on a per (sequence,
-// KV head) counter; the last group to arrive merges them (level 2) and writes out,
-// then returns the counter to zero. This replaces the merge launch and its dependent
-// loads, which dominate the time of such small calls.
+// whose whole KV fits in one pass of the GPU), on a plain grid. A workgroup is
+// FusedUnits units of GroupSplits waves, each unit one (sequence, group of GroupSplits
+// consecutive splits, KV head). With two units and an even KV-head count the units are
+// the two heads of a head pair over the same splits, on alternating waves, so both
+// halves of each token's K/V record are read by one CU at about the same time while
+// the two waves sharing a SIMD (w, w + 4) are two splits of one head, whose loads
+// arrive independently. On the FP8 64 x 8192 pools a read of the decode's bytes alone
+// took 47.3 us with one head per workgroup and 42.7 us with head pairs (a plain
+// streaming read of the same bytes: 42.3 us); the decode went from 56.2 to 54.3 us
+// (with the pair on one SIMD instead: 60.6 us). With an odd head count the two units
+// are two consecutive groups of one head. The item's query rows and block ids are requested before its
+// context length is known, each unit merges its waves' partials in LDS (level 1), and
+// a sequence with several groups publishes group partials to the workspace and counts
+// arrivals on a per (sequence, KV head) counter; the last group to arrive merges them
+// (level 2) and writes out, then returns the counter to zero. This replaces the merge
+// launch and its dependent loads, which dominate the time of such small calls.
 // STEP: a decode step (knew / vnew / slots set); a separate instantiation so that its
 // loads are issued with the others, not behind a branch.
 template <int KVT, int D, int G, int QT, bool STEP>
-__global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitArgs a) {
+__global__ void __launch_bounds__(64 * kFusedWaves) decode_fused_kernel(SplitArgs a) {
   using Gm = Geom<KVT, D>;
-  constexpr int NW = kGroupSplits;
+  constexpr int NW = kFusedWaves;
+  constexpr int NU = FusedUnits<KVT>::value;
+  constexpr int UW = GroupSplits<KVT>::value;  // waves per unit
   constexpr int D4 = D / 4;
-  static_assert(G * D4 <= 64 * NW, "one merge column per thread");
+  static_assert(G * D4 <= 64 * UW, "one merge column per thread of a unit");
   __shared__ float part_o[NW][G][D];
   __shared__ float part_lse[NW][G];
-  __shared__ unsigned arrival;
+  __shared__ unsigned arrival[2];
   __shared__ int progress[NW];  // blocks done per wave (issue fairness, see balance_issue)
   // Every kernel argument the launch uses, loaded up front: without this the compiler
   // loads them region by region behind divergent branches, and each region waited
@@ -1183,17 +1209,42 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
                "s"(a.vnew_sh), "s"(a.counters), "s"(a.ws_o), "s"(a.ws_lse),
                "s"(a.scale_log2), "s"((int)a.q_aligned), "s"((int)a.out_aligned));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // KV head slowest: consecutive workgroups go to different XCDs, so every XCD gets
-  // the same mix of heads (with the head fastest, an XCD would only see heads
+  // with two units the item's unit alternates with the wave (the two units' waves of
+  // one split sit on neighbouring SIMDs; the waves sharing a SIMD, w and w + 4, are two
+  // splits of one unit, whose loads arrive independently)
+  const int unit = NU == 2 ? wave & 1 : 0, wu = NU == 2 ? wave >> 1 : wave;
+  // KV head (pair) slowest: consecutive workgroups go to different XCDs, so every XCD
+  // gets the same mix of heads (with the head fastest, an XCD would only see heads
   // congruent to its index, and the FP8 64 x 8192 decode ran ~15% longer on KV head 1
   // than on head 0, which left the XCDs holding head 1 finishing last)
-  const int per_head = a.num_seqs * a.max_chunks;
-  const int g = (int)blockIdx.x / per_head;
-  const int rest = (int)blockIdx.x - g * per_head;
-  const int c = rest % a.max_chunks;
-  const int s = rest / a.max_chunks;
-  const int split = c * NW + wave;
-  static_assert(NW == 8, "balance_issue pairs wave w with w + 4");
+  // unit u is KV head g0 + u (head pairs) or group c0 + u (odd head counts)
+  const bool pairs = NU == 2 && (a.hkv & 1) == 0;
+  int s, g0, c0;
+  if (NU == 1) {
+    const int per_head = a.num_seqs * a.max_chunks;
+    g0 = (int)blockIdx.x / per_head;
+    const int rest = (int)blockIdx.x - g0 * per_head;
+    c0 = rest % a.max_chunks;
+    s = rest / a.max_chunks;
+  } else if (pairs) {
+    const int per_pair = a.num_seqs * a.max_chunks;
+    const int p = (int)blockIdx.x / per_pair;
+    const int rest = (int)blockIdx.x - p * per_pair;
+    c0 = rest % a.max_chunks;
+    s = rest / a.max_chunks;
+    g0 = 2 * p;
+  } else {
+    const int nc2 = (a.max_chunks + 1) / 2;
+    const int per_head = a.num_seqs * nc2;
+    g0 = (int)blockIdx.x / per_head;
+    const int rest = (int)blockIdx.x - g0 * per_head;
+    c0 = 2 * (rest % nc2);
+    s = rest / nc2;
+  }
+  const int g = pairs ? g0 + unit : g0;
+  const int c = pairs ? c0 : c0 + unit;
+  const int split = c * UW + wu;
+  static_assert(NW == 8 && NU * UW == NW, "balance_issue pairs wave w with w + 4: two splits of one unit");
   if (lane == 0)
     __hip_atomic_store(&progress[wave], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   // the context length and the step's slot, then the item's inputs: every request is
@@ -1213,7 +1264,7 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
   // nothing in this launch reads that pool slot, and the item does not wait for it.
   const char* krow_new = nullptr;
   const char* vrow_new = nullptr;
-  const bool copier = STEP && c == 0 && wave < 2 && lane < Gm::NCH;
+  const bool copier = STEP && c == 0 && wu < 2 && lane < Gm::NCH;
   uint4 new_row = make_uint4(0, 0, 0, 0);
   if constexpr (STEP) {
     krow_new = a.knew + ((int64_t)s * a.knew_st + (int64_t)g * a.knew_sh) * Gm::E;
@@ -1221,7 +1272,7 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
     // every lane loads (a chunk of its wave's row: in bounds), so no branch separates
     // this load from the others
     static_assert((Gm::NCH & (Gm::NCH - 1)) == 0, "chunks per row: a power of two");
-    new_row = *reinterpret_cast<const uint4*>(((wave & 1) ? vrow_new : krow_new) +
+    new_row = *reinterpret_cast<const uint4*>(((wu & 1) ? vrow_new : krow_new) +
                                               (lane & (Gm::NCH - 1)) * 16);
   }
   if (slot < 0) krow_new = vrow_new = nullptr;  // no new row: the pool holds the context
@@ -1229,16 +1280,19 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
     if (copier && slot >= 0 && slot < a.num_blocks * kBlockSize) {
       const int64_t off = (slot / kBlockSize) * kBlockSize * a.hkv * Gm::ROW +
                           ((slot % kBlockSize) * a.hkv + g) * Gm::ROW + lane * 16;
-      char* dst = const_cast<char*>(wave == 0 ? a.kpool : a.vpool) + off;
+      char* dst = const_cast<char*>(wu == 0 ? a.kpool : a.vpool) + off;
       *reinterpret_cast<uint4*>(dst) = new_row;
     }
   };
   const int nsplit = num_splits(L, a.split_tokens);
-  const int ngroups = (nsplit + NW - 1) / NW;
-  if (c >= ngroups) {  // uniform over the workgroup, before any barrier
+  const int ngroups = (nsplit + UW - 1) / UW;
+  if (c0 >= ngroups) {  // uniform over the workgroup, before any barrier
     copy_new_row();
     return;
   }
+  // (two units, odd head counts) unit 1 may be past the last group: its waves run
+  // empty items (splits past the context) through the barriers, and it publishes
+  // nothing
   float o[G][Gm::EV], lse2[G];
   if constexpr (MmaPath<KVT, G>::value) {
     // Every wave's progress word is written before any wave reads its partner's (the
@@ -1268,42 +1322,49 @@ __global__ void __launch_bounds__(64 * kGroupSplits) decode_fused_kernel(SplitAr
     for (int h = 0; h < G; ++h) part_lse[wave][h] = lse2[h];
   }
   __syncthreads();
-  const int t = threadIdx.x;
+  // merge: threads 256 mu .. 256 mu + 255 take unit mu, whose splits are waves mu + 2 i
+  // (two units), or all threads the one unit (waves 0..7)
+  const int mu = NU == 2 ? (int)threadIdx.x >> 8 : 0;
+  const int t = NU == 2 ? (int)threadIdx.x & 255 : (int)threadIdx.x;
+  const int mg = pairs ? g0 + mu : g0;
+  const int mc = pairs || NU == 1 ? c0 : c0 + mu;
+  const bool has = mc < ngroups;
   const bool col = t < G * D4;
   const int h = col ? t / D4 : 0, d = 4 * (t % D4);
-  const int qh = g * G + h;
+  const int qh = mg * G + h;
   Merge4 grp;
   grp.init();
   if (col) {
-    float lw[NW];
-    float4 ow[NW];
+    float lw[UW];
+    float4 ow[UW];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      lw[w] = part_lse[w][h];
-      ow[w] = *reinterpret_cast<const float4*>(&part_o[w][h][d]);
+    for (int w = 0; w < UW; ++w) {
+      lw[w] = part_lse[mu + NU * w][h];
+      ow[w] = *reinterpret_cast<const float4*>(&part_o[mu + NU * w][h][d]);
     }
 #pragma unroll
-    for (int w = 0; w < NW; ++w) grp.add(lw[w], ow[w]);
+    for (int w = 0; w < UW; ++w) grp.add(lw[w], ow[w]);
   }
-  if (ngroups == 1) {
-    if (col) store_out4<QT>(a.out, a.out_st, a.out_sh, a.out_aligned, s, qh, d, grp.acc, 1.0f / grp.den);
+  if (ngroups == 1) {  // then c == 0 for every unit that has work
+    if (col && has) store_out4<QT>(a.out, a.out_st, a.out_sh, a.out_aligned, s, qh, d, grp.acc, 1.0f / grp.den);
     return;
   }
   const int64_t row0 = ((int64_t)s * a.hkv * G + qh) * a.max_splits;
-  if (col) {
+  if (col && has) {
     const float inv = 1.0f / grp.den;
-    st_dev4(partial_rsrc(a, G, D), (uint32_t)(((row0 + c) * D + d) * 4), grp.acc[0] * inv,
+    st_dev4(partial_rsrc(a, G, D), (uint32_t)(((row0 + mc) * D + d) * 4), grp.acc[0] * inv,
             grp.acc[1] * inv, grp.acc[2] * inv, grp.acc[3] * inv);
-    if (d == 0) st_dev(a.ws_lse + row0 + c, grp.m + __log2f(grp.den));
+    if (d == 0) st_dev(a.ws_lse + row0 + mc, grp.m + __log2f(grp.den));
   }
   // every thread's partial stores have completed before the arrival is counted
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  unsigned* counter = a.counters + ((int64_t)s * a.hkv + g);
-  if (t == 0)
-    arrival = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned* counter = a.counters + ((int64_t)s * a.hkv + mg);
+  if (t == 0 && has)
+    arrival[mu] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (arrival != (unsigned)(ngroups - 1)) return;
+  // per unit from here on (no barrier follows)
+  if (!has || arrival[mu] != (unsigned)(ngroups - 1)) return;
   if (col) {
     Merge4 top;
     top.init();
@@ -1348,13 +1409,23 @@ static int launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, const 
   };
   sa.q_aligned = al(a.q, a.q_st, a.q_sh, qe);
   sa.out_aligned = al(a.out, a.out_st, a.out_sh, qe);
-  sa.max_chunks = (a.max_splits + kGroupSplits - 1) / kGroupSplits;
+  sa.group_splits = GroupSplits<KVT>::value;
+  sa.max_chunks = (a.max_splits + sa.group_splits - 1) / sa.group_splits;
   sa.counters = a.counters;
   sa.knew = sa.vnew = nullptr;
   sa.knew_st = sa.knew_sh = sa.vnew_st = sa.vnew_sh = 0;
   sa.slots = nullptr;
-  const int64_t fused_groups = (int64_t)a.num_seqs * pool.kv_heads * sa.max_chunks;
-  if (step != nullptr && fused_groups <= kFusedMaxWorkgroups) {
+  // single-launch workgroups: (sequence, head, group); with two units (sequence, head
+  // pair, group) or (sequence, head, two groups)
+  const int64_t fused_groups =
+      FusedUnits<KVT>::value == 1 ? (int64_t)a.num_seqs * pool.kv_heads * sa.max_chunks
+      : pool.kv_heads % 2 == 0    ? (int64_t)a.num_seqs * (pool.kv_heads / 2) * sa.max_chunks
+                                  : (int64_t)a.num_seqs * pool.kv_heads * ((sa.max_chunks + 1) / 2);
+  // its arrival counters (one per (sequence, KV head), used when there are two or more
+  // groups) stay below the persistent schedule's two words
+  const bool fused = fused_groups <= kFusedMaxWorkgroups &&
+                     (sa.max_chunks == 1 || (int64_t)a.num_seqs * pool.kv_heads <= kCompactQueueWord);
+  if (step != nullptr && fused) {
     sa.knew = (const char*)step->k;
     sa.vnew = (const char*)step->v;
     sa.knew_st = step->k_st;
@@ -1367,13 +1438,12 @@ static int launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, const 
                                 step->k_sh, step->v_st, step->v_sh, step->slots, stream);
     if (st != PA_OK) return st;
   }
-  static_assert(kFusedMaxWorkgroups <= kDecodeCounters, "one counter per (sequence, KV head)");
-  if (fused_groups <= kFusedMaxWorkgroups) {
+  if (fused) {
     if (sa.knew != nullptr)
-      decode_fused_kernel<KVT, D, G, QT, true><<<(unsigned)fused_groups, 64 * kGroupSplits, 0,
+      decode_fused_kernel<KVT, D, G, QT, true><<<(unsigned)fused_groups, 64 * kFusedWaves, 0,
                                                  stream>>>(sa);
     else
-      decode_fused_kernel<KVT, D, G, QT, false><<<(unsigned)fused_groups, 64 * kGroupSplits, 0,
+      decode_fused_kernel<KVT, D, G, QT, false><<<(unsigned)fused_groups, 64 * kFusedWaves, 0,
                                                   stream>>>(sa);
     return PA_OK;
   }
