@@ -42,6 +42,8 @@
 namespace pa {
 
 constexpr int kWaves = 4;  // wavefronts (independent work items) per 256-thread block
+// Most waves of any workgroup that runs decode_item (the persistent schedule's 8).
+constexpr int kMaxItemWaves = 8;
 constexpr int kRowMirror = 0x140;
 constexpr int kHalfMirror = 0x141;
 
@@ -788,7 +790,7 @@ __device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split
   float o[G][Gm::EV], lse2[G];
   int nsplit;
   if constexpr (MmaPath<KVT, G>::value) {
-    __shared__ float stage[kWaves][G][D];
+    __shared__ float stage[kMaxItemWaves][G][D];  // one slice per wave of the workgroup
     MmaIn<D> in;
     load_mma_inputs<ElemBytes<KVT>::value, D, G>(a, s, split, g, lane, in);
     const int L = clamped_len(a, s);
@@ -861,7 +863,7 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(SplitArgs a) 
 
 // Compact persistent schedule. Every workgroup prefix-sums the per-sequence split
 // counts into LDS, which enumerates exactly the existing (sequence, split, kv head)
-// items (kv head fastest, four per workgroup step); workgroup b then walks the b-th
+// items (kv head fastest, eight per workgroup step); workgroup b then walks the b-th
 // contiguous share of them. Dispatching only real work matters for skewed batches:
 // padding the grid to max_context_len would launch mostly empty workgroups.
 constexpr int kMaxCompactSeqs = 4096;
@@ -892,6 +894,7 @@ constexpr int64_t kFusedMaxWorkgroups = 1024;
 constexpr int kCompactQueueWord = kDecodeCounters - 2;
 constexpr int kCompactDoneWord = kDecodeCounters - 1;
 
+template <int NWAVES>
 __device__ __forceinline__ int block_exclusive_scan(int x, int* wave_sums, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = x;
@@ -905,7 +908,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* wave_sums, int& 
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NWAVES; ++w) {
     const int v = wave_sums[w];
     before += w < wave ? v : 0;
     total += v;
@@ -914,28 +917,35 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* wave_sums, int& 
   return before + incl - x;
 }
 
+// Waves (items) per workgroup step of the persistent schedule. Items are enumerated
+// KV head fastest, so a step of eight holds all heads of a (sequence, split) at eight
+// KV heads (pairs of heads at two): a CU reads whole token records of the pool, not
+// halves of them, at the same occupancy as two four-wave workgroups.
+constexpr int kCompactWaves = 8;
+static_assert(kCompactWaves <= kMaxItemWaves && kWaves <= kMaxItemWaves, "decode_item's LDS slices");
+
 template <int KVT, int D, int G, int QT>
-__global__ void __launch_bounds__(64 * kWaves, (MmaPath<KVT, G>::value) ? 2 : 1)
+__global__ void __launch_bounds__(64 * kCompactWaves, 1)
     decode_compact_kernel(SplitArgs a) {
   __shared__ int cum[kMaxCompactSeqs + 1];  // cum[s] = splits of sequences before s
-  __shared__ int wave_sums[kWaves];
+  __shared__ int wave_sums[kCompactWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int carry = 0;
-  for (int base = 0; base < a.num_seqs; base += 64 * kWaves) {
+  for (int base = 0; base < a.num_seqs; base += 64 * kCompactWaves) {
     const int s = base + (int)threadIdx.x;
     const int n = s < a.num_seqs ? num_splits(clamped_len(a, s), a.split_tokens) : 0;
     int tot;
-    const int ex = block_exclusive_scan(n, wave_sums, tot);
+    const int ex = block_exclusive_scan<kCompactWaves>(n, wave_sums, tot);
     if (s < a.num_seqs) cum[s] = carry + ex;
     carry += tot;
   }
   if (threadIdx.x == 0) cum[a.num_seqs] = carry;
   __syncthreads();
   const int64_t entries = (int64_t)carry * a.hkv;
-  const int64_t steps = (entries + kWaves - 1) / kWaves;
-  // the four items of workgroup step st (one per wave)
+  const int64_t steps = (entries + kCompactWaves - 1) / kCompactWaves;
+  // the items of workgroup step st (one per wave)
   auto run_step = [&](int64_t st) {
-    const int64_t e = st * kWaves + wave;
+    const int64_t e = st * kCompactWaves + wave;
     if (e >= entries) return;
     const int g = (int)(e % a.hkv);
     const int pair = (int)(e / a.hkv);
@@ -1448,12 +1458,13 @@ static int launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, const 
     return PA_OK;
   }
   const int64_t items = (int64_t)a.num_seqs * a.max_splits * pool.kv_heads;
-  const int64_t steps = (items + kWaves - 1) / kWaves;  // upper bound of workgroup steps
   if (a.num_seqs <= kMaxCompactSeqs) {
+    const int64_t steps = (items + kCompactWaves - 1) / kCompactWaves;  // upper bound
     auto kern = decode_compact_kernel<KVT, D, G, QT>;
-    const int64_t grid = std::min(steps, resident_workgroups(kern, 64 * kWaves));
-    kern<<<(unsigned)grid, 64 * kWaves, 0, stream>>>(sa);
+    const int64_t grid = std::min(steps, resident_workgroups(kern, 64 * kCompactWaves));
+    kern<<<(unsigned)grid, 64 * kCompactWaves, 0, stream>>>(sa);
   } else {
+    const int64_t steps = (items + kWaves - 1) / kWaves;
     decode_split_kernel<KVT, D, G, QT><<<(unsigned)steps, 64 * kWaves, 0, stream>>>(sa);
   }
   if (a.max_splits > 1)
