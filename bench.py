@@ -36,10 +36,13 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, datasheet
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, datasheet
 LAYERS = 28                      # Qwen2.5-1.5B's layer count (public model config)
 PROFILES = os.path.join(ROOT, "profiles")
+# sources whose text decides a recorded kernel's traffic (api.cpp: split policy and
+# workspace layout)
 DECODE_SOURCES = ["paged_kv_cache_95_amd/csrc/decode.hip", "paged_kv_cache_95_amd/csrc/common.h",
-                  "paged_kv_cache_95_amd/csrc/internal.h"]
+                  "paged_kv_cache_95_amd/csrc/internal.h", "paged_kv_cache_95_amd/csrc/api.cpp"]
 PREFILL_SOURCES = ["paged_kv_cache_95_amd/csrc/prefill.hip",
-                   "paged_kv_cache_95_amd/csrc/common.h", "paged_kv_cache_95_amd/csrc/internal.h"]
+                   "paged_kv_cache_95_amd/csrc/common.h", "paged_kv_cache_95_amd/csrc/internal.h",
+                   "paged_kv_cache_95_amd/csrc/api.cpp"]
 WORKLOADS = ("large_decode", "qwen_step", "fp8_decode", "int8_decode", "varlen_prefill", "copy")
 
 

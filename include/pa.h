@@ -238,7 +238,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t q_heads, int32_t kv_h
                                  int32_t split_tokens);
 
 /* Split length (tokens) pa_decode uses for split_tokens == 0 with this call shape: the
- * power of two in [32, 512] nearest above num_seqs*kv_heads*max_context_len/2048, so
+ * power of two in [32, 1024] nearest above num_seqs*kv_heads*max_context_len/2048, so
  * that a worst-case batch has about 2048 (sequence, KV head, split) work items. Returns
  * 0 for non-positive arguments. */
 int32_t pa_decode_default_split_tokens(int32_t num_seqs, int32_t kv_heads,

@@ -70,7 +70,7 @@ int abi_cases() {
       {pa_copy_blocks(&p, nullptr, cl, 3, nullptr), PA_ERR_INVALID_ARG},
       {(int)pa_decode_workspace_bytes(2, 12, 2, 128, 128, 16) == 4096 + 2 * 12 * 8 * 129 * 4 ? PA_OK : -99, PA_OK},
       {(int)pa_decode_workspace_bytes(-2, 12, 2, 128, 128, 16), 0},
-      {pa_decode_default_split_tokens(256, 8, 32768), 512},
+      {pa_decode_default_split_tokens(256, 8, 32768), 1024},
   };
   int i = 0;
   for (const Case& c : cases) {

@@ -179,7 +179,9 @@ def test_default_split_and_workspace_bytes(lib):
     assert ds(8, 2, 3200) == 32            # small batch: short splits
     assert ds(8, 2, 8192) == 64
     assert ds(64, 2, 8192) == 512
-    assert ds(256, 8, 32768) == 512        # capped
+    assert ds(256, 8, 32768) == 1024       # capped
+    assert ds(16, 8, 4096) == 256
+    assert ds(64, 8, 8192) == 1024
     assert ds(16, 8, 8192) == 512
     assert ds(8, 8, 8192) == 256
     assert ds(0, 2, 100) == 0
