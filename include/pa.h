@@ -89,7 +89,9 @@ enum {
   PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad stride, bad dtype combo */
   PA_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, block_size, group size */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_bytes() */
-  PA_ERR_HIP = -4,         /* a kernel launch failed */
+  PA_ERR_HIP = -4,         /* one of this call's kernel launches failed (each launch's own
+                              status; an error pending from the caller's earlier HIP
+                              calls is neither reported nor cleared) */
   PA_ERR_DEVICE_DATA = -5  /* PA_DEBUG_CHECKS build only: an earlier call's device-side
                               metadata broke its contract (pa_debug_take_violation) */
 };

@@ -61,10 +61,10 @@ int check_store_rows(const pa_kv_pool_t* pool, int32_t src_dtype, int64_t k_stri
   return PA_OK;
 }
 
-int launched(int status) {
-  if (status != PA_OK) return status;
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
-}
+// Status of an entry point's launches: each launch reports its own status (see
+// launch_kernel), so an error left pending by the caller's earlier HIP calls is neither
+// attributed to this call nor cleared.
+int launched(int status) { return status; }
 
 // PA_DEBUG_CHECKS build: before a call launches, wait for its stream and refuse it while
 // an earlier call's violation is recorded, then launch the check of this call's device

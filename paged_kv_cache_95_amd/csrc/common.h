@@ -1,12 +1,34 @@
 // Device helpers shared by the paged-attention kernels (gfx950 / CDNA4, wave64).
 #pragma once
 
+#include <tuple>
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/pa.h"
 
 namespace pa {
+
+// Launch `kernel` on `stream` and return this launch's own status (hipLaunchKernel's),
+// so that an error left pending by the caller's earlier HIP calls is neither reported
+// for this launch nor cleared. The arguments are converted to the kernel's parameter
+// types first.
+template <typename... P, typename... A>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                                A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+  std::tuple<std::decay_t<P>...> vals(std::forward<A>(args)...);
+  void* argv[sizeof...(P) > 0 ? sizeof...(P) : 1] = {};
+  std::apply(
+      [&argv](auto&... v) {
+        int i = 0;
+        ((argv[i++] = static_cast<void*>(&v)), ...);
+      },
+      vals);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream);
+}
+
 
 // ------------------------------------------------------------------ element traits
 // KV element kinds (same numbering as the PA_* dtype enum).

@@ -1449,28 +1449,31 @@ static int launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, const 
     if (st != PA_OK) return st;
   }
   if (fused) {
-    if (sa.knew != nullptr)
-      decode_fused_kernel<KVT, D, G, QT, true><<<(unsigned)fused_groups, 64 * kFusedWaves, 0,
-                                                 stream>>>(sa);
-    else
-      decode_fused_kernel<KVT, D, G, QT, false><<<(unsigned)fused_groups, 64 * kFusedWaves, 0,
-                                                  stream>>>(sa);
-    return PA_OK;
+    const hipError_t e =
+        sa.knew != nullptr
+            ? launch_kernel(decode_fused_kernel<KVT, D, G, QT, true>, dim3((unsigned)fused_groups),
+                            dim3(64 * kFusedWaves), stream, sa)
+            : launch_kernel(decode_fused_kernel<KVT, D, G, QT, false>, dim3((unsigned)fused_groups),
+                            dim3(64 * kFusedWaves), stream, sa);
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
   const int64_t items = (int64_t)a.num_seqs * a.max_splits * pool.kv_heads;
+  hipError_t e;
   if (a.num_seqs <= kMaxCompactSeqs) {
     const int64_t steps = (items + kCompactWaves - 1) / kCompactWaves;  // upper bound
     auto kern = decode_compact_kernel<KVT, D, G, QT>;
     const int64_t grid = std::min(steps, resident_workgroups(kern, 64 * kCompactWaves));
-    kern<<<(unsigned)grid, 64 * kCompactWaves, 0, stream>>>(sa);
+    e = launch_kernel(kern, dim3((unsigned)grid), dim3(64 * kCompactWaves), stream, sa);
   } else {
     const int64_t steps = (items + kWaves - 1) / kWaves;
-    decode_split_kernel<KVT, D, G, QT><<<(unsigned)steps, 64 * kWaves, 0, stream>>>(sa);
+    e = launch_kernel(decode_split_kernel<KVT, D, G, QT>, dim3((unsigned)steps),
+                      dim3(64 * kWaves), stream, sa);
   }
-  if (a.max_splits > 1)
-    decode_merge_kernel<D, G, QT><<<(unsigned)((int64_t)a.num_seqs * pool.kv_heads),
-                                    kMergeThreads, 0, stream>>>(sa);
-  return PA_OK;
+  if (e == hipSuccess && a.max_splits > 1)
+    e = launch_kernel(decode_merge_kernel<D, G, QT>,
+                      dim3((unsigned)((int64_t)a.num_seqs * pool.kv_heads)), dim3(kMergeThreads),
+                      stream, sa);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 template <int KVT, int D, int QT>
@@ -1544,8 +1547,9 @@ int noalloc_scratch(void** ptr, hipStream_t stream) {
     // its first use (every call leaves them zero again); a kernel, not a memset, so that
     // a first call under graph capture records an ordinary kernel node
     constexpr int words = (int)(kDecodeCounterBytes / sizeof(unsigned));
-    zero_words_kernel<<<(words + 255) / 256, 256, 0, stream>>>((unsigned*)p, words);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    if (launch_kernel(zero_words_kernel, dim3((words + 255) / 256), dim3(256), stream,
+                      (unsigned*)p, words) != hipSuccess)
+      return PA_ERR_HIP;
     dev_ptr[dev] = p;
   }
   *ptr = dev_ptr[dev];

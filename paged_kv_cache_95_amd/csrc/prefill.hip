@@ -661,7 +661,7 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PfArgs a) {
 }
 
 template <int D, int G>
-static void launch_prefill_t(const pa_kv_pool_t& pool, const PrefillArgs& pa_, hipStream_t stream) {
+static int launch_prefill_t(const pa_kv_pool_t& pool, const PrefillArgs& pa_, hipStream_t stream) {
   PfArgs a;
   a.kpool = (const uint16_t*)pool.k;
   a.vpool = (const uint16_t*)pool.v;
@@ -691,28 +691,33 @@ static void launch_prefill_t(const pa_kv_pool_t& pool, const PrefillArgs& pa_, h
   a.plan_bound = pa_.plan_bound;
   a.ws_o = pa_.ws_o;
   a.ws_lse = pa_.ws_lse;
-  prefill_plan_kernel<<<1, kPfPlanThreads, 0, stream>>>(a);
+  if (launch_kernel(prefill_plan_kernel, dim3(1), dim3(kPfPlanThreads), stream, a) != hipSuccess)
+    return PA_ERR_HIP;
   // persistent: no more workgroups than fit at once, nor than there are work items
   const int64_t items = (int64_t)a.tiles_per_seq * a.max_chunks * pool.kv_heads * pa_.num_seqs;
   const int64_t grid = std::min(items, resident_workgroups(prefill_kernel<D, G>, 256));
-  prefill_kernel<D, G><<<(unsigned)grid, 256, 0, stream>>>(a);
-  if (a.max_chunks > 1)
-    prefill_merge_kernel<D><<<(unsigned)((int64_t)(kPfRows / pf_merge_rows<D>()) *
-                                         a.tiles_per_seq * pool.kv_heads * pa_.num_seqs),
-                              256, 0, stream>>>(a);
+  if (launch_kernel(prefill_kernel<D, G>, dim3((unsigned)grid), dim3(256), stream, a) != hipSuccess)
+    return PA_ERR_HIP;
+  if (a.max_chunks > 1 &&
+      launch_kernel(prefill_merge_kernel<D>,
+                    dim3((unsigned)((int64_t)(kPfRows / pf_merge_rows<D>()) * a.tiles_per_seq *
+                                    pool.kv_heads * pa_.num_seqs)),
+                    dim3(256), stream, a) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
 }
 
 template <int D>
 static int dispatch_pf_g(const pa_kv_pool_t& pool, const PrefillArgs& a, hipStream_t stream) {
   switch (a.q_heads / pool.kv_heads) {
-    case 1: launch_prefill_t<D, 1>(pool, a, stream); return PA_OK;
-    case 2: launch_prefill_t<D, 2>(pool, a, stream); return PA_OK;
-    case 3: launch_prefill_t<D, 3>(pool, a, stream); return PA_OK;
-    case 4: launch_prefill_t<D, 4>(pool, a, stream); return PA_OK;
-    case 5: launch_prefill_t<D, 5>(pool, a, stream); return PA_OK;
-    case 6: launch_prefill_t<D, 6>(pool, a, stream); return PA_OK;
-    case 7: launch_prefill_t<D, 7>(pool, a, stream); return PA_OK;
-    case 8: launch_prefill_t<D, 8>(pool, a, stream); return PA_OK;
+    case 1: return launch_prefill_t<D, 1>(pool, a, stream);
+    case 2: return launch_prefill_t<D, 2>(pool, a, stream);
+    case 3: return launch_prefill_t<D, 3>(pool, a, stream);
+    case 4: return launch_prefill_t<D, 4>(pool, a, stream);
+    case 5: return launch_prefill_t<D, 5>(pool, a, stream);
+    case 6: return launch_prefill_t<D, 6>(pool, a, stream);
+    case 7: return launch_prefill_t<D, 7>(pool, a, stream);
+    case 8: return launch_prefill_t<D, 8>(pool, a, stream);
     default: return PA_ERR_UNSUPPORTED;
   }
 }

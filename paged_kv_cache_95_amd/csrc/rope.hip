@@ -121,7 +121,9 @@ int launch_rope_store(const pa_kv_pool_t& pool, const RopeArgs& a, int src_dtype
   int64_t grid = (rows * 16 + 255) / 256;
   grid = grid < 1 ? 1 : (grid > 256 * 64 ? 256 * 64 : grid);
   const int D = pool.head_dim;
-#define PA_ROPE(S, DD, P) rope_store_kernel<S, DD, P><<<(unsigned)grid, 256, 0, stream>>>(a)
+  hipError_t e = hipSuccess;
+#define PA_ROPE(S, DD, P) \
+  e = launch_kernel(rope_store_kernel<S, DD, P>, dim3((unsigned)grid), dim3(256), stream, a)
 #define PA_ROPE_P(S, DD)                                                   \
   switch (pool.dtype) {                                                    \
     case PA_F32: PA_ROPE(S, DD, kF32); break;                              \
@@ -137,7 +139,7 @@ int launch_rope_store(const pa_kv_pool_t& pool, const RopeArgs& a, int src_dtype
   }
 #undef PA_ROPE_P
 #undef PA_ROPE
-  return PA_OK;
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // namespace pa

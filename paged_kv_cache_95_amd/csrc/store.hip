@@ -162,10 +162,11 @@ int launch_store(const pa_kv_pool_t& pool, const void* k, const void* v, int src
   const int hkv = pool.kv_heads, D = pool.head_dim;
   if (pool.dtype == PA_FP8_E4M3 || pool.dtype == PA_INT8) {
     const int grid = grid_for(2 * num_tokens * hkv * 16, 256);
+    hipError_t e = hipSuccess;
 #define PA_QUANT_STORE(SRC, DD, Q)                                                          \
-  store_quant_kernel<SRC, DD, Q><<<grid, 256, 0, stream>>>(                                \
-      (uint8_t*)pool.k, (uint8_t*)pool.v, pool.k_scale, pool.v_scale, k, v, k_st, k_sh,    \
-      v_st, v_sh, slot_mapping, num_tokens, hkv, num_slots)
+  e = launch_kernel(store_quant_kernel<SRC, DD, Q>, dim3(grid), dim3(256), stream,         \
+                    (uint8_t*)pool.k, (uint8_t*)pool.v, pool.k_scale, pool.v_scale, k, v,  \
+                    k_st, k_sh, v_st, v_sh, slot_mapping, num_tokens, hkv, num_slots)
 #define PA_QUANT_STORE_Q(Q)                                                                 \
     if (src_dtype == PA_BF16 && D == 128) PA_QUANT_STORE(kBF16, 128, Q);                    \
     else if (src_dtype == PA_BF16 && D == 64) PA_QUANT_STORE(kBF16, 64, Q);                 \
@@ -179,7 +180,7 @@ int launch_store(const pa_kv_pool_t& pool, const void* k, const void* v, int src
     }
 #undef PA_QUANT_STORE_Q
 #undef PA_QUANT_STORE
-    return PA_OK;
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
   const int E = pool.dtype == PA_F32 ? 4 : 2;
   const int row_bytes = D * E;
@@ -187,28 +188,20 @@ int launch_store(const pa_kv_pool_t& pool, const void* k, const void* v, int src
   const bool vec16 = al16(k) && al16(v) && al16(pool.k) && al16(pool.v) &&
                      ((k_st * E) % 16 == 0) && ((k_sh * E) % 16 == 0) &&
                      ((v_st * E) % 16 == 0) && ((v_sh * E) % 16 == 0);
+  auto copy = [&](auto kernel, int grid) {
+    return launch_kernel(kernel, dim3(grid), dim3(256), stream, (char*)pool.k, (char*)pool.v,
+                         (const char*)k, (const char*)v, k_st, k_sh, v_st, v_sh, slot_mapping,
+                         num_tokens, hkv, row_bytes, num_slots);
+  };
+  hipError_t e;
   if (vec16) {
     const int grid = grid_for(2 * num_tokens * hkv * (row_bytes / 16), 256);
-    if (E == 4)
-      store_copy_kernel<16, 4><<<grid, 256, 0, stream>>>(
-          (char*)pool.k, (char*)pool.v, (const char*)k, (const char*)v, k_st, k_sh, v_st, v_sh,
-          slot_mapping, num_tokens, hkv, row_bytes, num_slots);
-    else
-      store_copy_kernel<16, 2><<<grid, 256, 0, stream>>>(
-          (char*)pool.k, (char*)pool.v, (const char*)k, (const char*)v, k_st, k_sh, v_st, v_sh,
-          slot_mapping, num_tokens, hkv, row_bytes, num_slots);
+    e = E == 4 ? copy(store_copy_kernel<16, 4>, grid) : copy(store_copy_kernel<16, 2>, grid);
   } else {
     const int grid = grid_for(2 * num_tokens * hkv * (row_bytes / E), 256);
-    if (E == 4)
-      store_copy_kernel<4, 4><<<grid, 256, 0, stream>>>(
-          (char*)pool.k, (char*)pool.v, (const char*)k, (const char*)v, k_st, k_sh, v_st, v_sh,
-          slot_mapping, num_tokens, hkv, row_bytes, num_slots);
-    else
-      store_copy_kernel<2, 2><<<grid, 256, 0, stream>>>(
-          (char*)pool.k, (char*)pool.v, (const char*)k, (const char*)v, k_st, k_sh, v_st, v_sh,
-          slot_mapping, num_tokens, hkv, row_bytes, num_slots);
+    e = E == 4 ? copy(store_copy_kernel<4, 4>, grid) : copy(store_copy_kernel<2, 2>, grid);
   }
-  return PA_OK;
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 int launch_copy_blocks(const pa_kv_pool_t& pool, const int32_t* src, const int32_t* dst, int n,
@@ -218,10 +211,10 @@ int launch_copy_blocks(const pa_kv_pool_t& pool, const int32_t* src, const int32
   const bool quant = pool.dtype == PA_FP8_E4M3 || pool.dtype == PA_INT8;
   const int spb = quant ? pool.block_size * pool.kv_heads : 0;
   const int grid = grid_for((int64_t)n * (2 * block_bytes / 16 + 2 * spb), 256);
-  copy_blocks_kernel<<<grid, 256, 0, stream>>>((char*)pool.k, (char*)pool.v, pool.k_scale,
-                                               pool.v_scale, src, dst, n, pool.num_blocks,
-                                               block_bytes, spb);
-  return PA_OK;
+  const hipError_t e = launch_kernel(copy_blocks_kernel, dim3(grid), dim3(256), stream,
+                                     (char*)pool.k, (char*)pool.v, pool.k_scale, pool.v_scale,
+                                     src, dst, n, pool.num_blocks, block_bytes, spb);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // namespace pa

@@ -159,9 +159,10 @@ int validate_decode(const pa_kv_pool_t& pool, const int32_t* block_tables, int m
   unsigned long long* w = nullptr;
   const int st = violation_ptr(&w);
   if (st != PA_OK) return st;
-  validate_decode_kernel<<<num_seqs, 64, 0, stream>>>(block_tables, max_blocks, ctx, max_ctx,
-                                                      pool.num_blocks, slots, w);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  const hipError_t e = launch_kernel(validate_decode_kernel, dim3(num_seqs), dim3(64), stream,
+                                     block_tables, max_blocks, ctx, max_ctx, pool.num_blocks,
+                                     slots, w);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 int validate_tokens(const pa_kv_pool_t& pool, const int64_t* slots, int64_t n,
@@ -170,19 +171,20 @@ int validate_tokens(const pa_kv_pool_t& pool, const int64_t* slots, int64_t n,
   const int st = violation_ptr(&w);
   if (st != PA_OK) return st;
   const int64_t grid = std::min<int64_t>((n + 255) / 256, 4096);
-  validate_tokens_kernel<<<(unsigned)grid, 256, 0, stream>>>(slots, n, pool.num_blocks,
-                                                             positions, max_position, w);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  const hipError_t e = launch_kernel(validate_tokens_kernel, dim3((unsigned)grid), dim3(256),
+                                     stream, slots, n, pool.num_blocks, positions, max_position, w);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 int validate_varlen(const pa_kv_pool_t& pool, const PrefillArgs& a, hipStream_t stream) {
   unsigned long long* w = nullptr;
   const int st = violation_ptr(&w);
   if (st != PA_OK) return st;
-  validate_varlen_kernel<<<a.num_seqs, 64, 0, stream>>>(
-      a.cu_seqlens, a.num_seqs, a.total_tokens, a.max_q_len, a.block_tables,
-      a.max_blocks_per_seq, a.context_lens, a.max_context_len, pool.num_blocks, w);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  const hipError_t e = launch_kernel(validate_varlen_kernel, dim3(a.num_seqs), dim3(64), stream,
+                                     a.cu_seqlens, a.num_seqs, a.total_tokens, a.max_q_len,
+                                     a.block_tables, a.max_blocks_per_seq, a.context_lens,
+                                     a.max_context_len, pool.num_blocks, w);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // namespace pa

@@ -412,3 +412,31 @@ def test_quantised_error_against_bf16_source_reported(dev, kv):
     print(f"{kv} decode against the bf16 source: max {d.max():.3e}, mean {d.mean():.3e}",
           flush=True)
     assert np.isfinite(d).all()  # reported only
+
+
+def test_pending_hip_error_of_the_caller_is_not_this_calls(dev):
+    """Each launch reports its own status: an error the caller's earlier HIP call left
+    pending (a failed allocation here) neither makes a decode call fail nor is cleared
+    by it. Everything is allocated first, so only the library runs in between."""
+    import ctypes
+    case = W.random_case(72, B=6, Hq=8, Hkv=2, D=128, lmin=1, lmax=600)
+    s = Setup(case, dev)
+    exp = s.oracle()
+    out = torch.empty_like(s.q)
+    ws = pa.decode_workspace(case.num_seqs, case.Hq, case.Hkv, case.D, case.max_context_len,
+                             device=dev)
+    torch.cuda.synchronize()
+    # the HIP runtime instance the library itself uses (dlsym through its handle)
+    hip = ctypes.CDLL(pa.LIB_PATH)
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    hip.hipMalloc.restype = ctypes.c_int
+    hip.hipGetLastError.restype = ctypes.c_int
+    ptr = ctypes.c_void_p()
+    failed = hip.hipMalloc(ctypes.byref(ptr), 1 << 60)  # refused: nothing allocated
+    assert failed != 0
+    pa.decode(s.q, s.pool, s.bt, s.ctx, case.scale, max_context_len=case.max_context_len,
+              out=out, workspace=ws)  # raises PaError on a non-OK status
+    left = hip.hipGetLastError()  # read (and clear) before torch's next HIP call
+    assert left == failed
+    torch.cuda.synchronize()
+    assert max_err(out, exp) <= TOL["bf16"]
