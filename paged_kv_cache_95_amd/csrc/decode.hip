@@ -1269,7 +1269,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) decode_fused_kernel(SplitArg
   asm volatile("" ::"s"(L_raw), "s"(slot));  // the first use of either value
   const int L = min(L_raw, a.max_context_len);
   // Decode step: every wave reads the new K/V row from the input, not from the pool,
-  // and group 0 of (s, g) copies it into the pool (waves 0 and 1, 16 bytes per lane).
+  // and the unit holding group 0 of (s, g) copies it into the pool (its first two
+  // waves: K, then V; 16 bytes per lane).
   // The copy's load goes out with the item's inputs and its store after the item:
   // nothing in this launch reads that pool slot, and the item does not wait for it.
   const char* krow_new = nullptr;
