@@ -440,3 +440,25 @@ def test_pending_hip_error_of_the_caller_is_not_this_calls(dev):
     assert left == failed
     torch.cuda.synchronize()
     assert max_err(out, exp) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kv", ["fp8", "int8"])
+@pytest.mark.parametrize("Hkv", [3, 4])
+def test_quantised_units_beyond_the_first_head_pair(dev, kv, Hkv):
+    """Quantised pools run two units per single-launch workgroup: head pairs (g0 = 2 at
+    four KV heads) or, at three, two consecutive groups of one head (the upper unit
+    past the last group for some lengths). Against the oracle, and each sequence alone
+    on the single launch bit-identical to the batch on the persistent schedule."""
+    B, Hq = 40, 2 * Hkv
+    case = W.random_case(73 + Hkv, B=B, Hq=Hq, Hkv=Hkv, D=128, kv_dtype=kv, lmin=1, lmax=1500)
+    s = Setup(case, dev)
+    ws = pa.decode_workspace(B, Hq, Hkv, 128, 1500, 16, device=dev)
+    out = pa.decode(s.q, s.pool, s.bt, s.ctx, case.scale, max_context_len=1500,
+                    split_tokens=16, workspace=ws)  # too many groups: persistent + merge
+    torch.cuda.synchronize()
+    assert max_err(out, s.oracle()) <= TOL[kv]
+    for b in sorted({0, 1, B - 1, int(np.argmin(case.context_lens)),
+                     int(np.argmax(case.context_lens))}):
+        o1 = pa.decode(s.q[b:b + 1], s.pool, s.bt[b:b + 1], s.ctx[b:b + 1], case.scale,
+                       max_context_len=1500, split_tokens=16, workspace=ws)
+        assert torch.equal(o1[0], out[b]), b
