@@ -5,7 +5,7 @@
 
 Headline workload (one "step"): the large decode batch. 256 sequences, 32 query / 8 KV
 heads, head_dim 128, bf16 KV in 16-token blocks, contexts log-uniform in [1024, 32768]
-(seeded; about 2.3M tokens, 9.6 GB of KV, far more than the 256 MB MALL). A step
+(seeded; 2.69M context tokens, 11.0 GB of KV, far more than the 256 MB MALL). A step
 stores each sequence's new K/V row through slot_mapping and then attends the whole
 context (pa_decode_step: a store launch, the persistent split-K decode kernel and the
 log-sum-exp merge). The step is captured once in a HIP graph and replayed, so the
