@@ -142,8 +142,12 @@ enum {
                                    chunk longer than max_q_len; where = s */
   PA_VIOLATION_STEP_SLOT = 6,   /* pa_decode_step: slot_mapping[s] >= 0 but not the slot of
                                    position context_lens[s] - 1; where = s */
-  PA_VIOLATION_POSITION = 7     /* pa_rope_store_kv: positions[t] outside [0, max_position);
+  PA_VIOLATION_POSITION = 7,    /* pa_rope_store_kv: positions[t] outside [0, max_position);
                                    where = t */
+  PA_VIOLATION_DUP_SLOT = 8     /* a slot named twice in one call's slot_mapping (store, RoPE
+                                   store, decode step; its rows would race); where = t, one
+                                   of the tokens naming it (whichever the parallel check
+                                   found second). Checked for calls of up to 2^19 tokens. */
 };
 /* 1 in the PA_DEBUG_CHECKS build, 0 in the release build. */
 int32_t pa_debug_checks(void);

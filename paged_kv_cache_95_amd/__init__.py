@@ -28,7 +28,7 @@ PA_ERR_DEVICE_DATA = -5
 BLOCK_SIZE = 16
 # contract violations a PA_DEBUG_CHECKS build records (pa.h)
 VIOLATIONS = {1: "context_len", 2: "block_id", 3: "slot", 4: "chunk", 5: "cu_seqlens",
-              6: "step_slot", 7: "position"}
+              6: "step_slot", 7: "position", 8: "dup_slot"}
 # bytes of the per-GPU scratch array behind decode_noalloc (PA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 

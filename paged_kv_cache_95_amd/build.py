@@ -21,6 +21,9 @@ OUT = os.path.join(HERE, "libpa.so")
 OUT_DEBUG = os.path.join(HERE, "libpa_debug.so")
 # the source compiled a second time, with -DPA_DEBUG_CHECKS, for libpa_debug.so
 DEBUG_LAYER = "api.cpp"
+# sources linked into libpa_debug.so only (the device-data checks and their per-GPU
+# state; the release layer never calls them)
+DEBUG_ONLY = ("validate.hip",)
 BUILD_DIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
@@ -75,7 +78,7 @@ def build(jobs=None, verbose=True):
         dbg = [ex.submit(compile_one, f, True) for f in debug_src]
         objs = [futs[f].result() for f in srcs]
         dbg_objs = [d.result() for d in dbg]
-    link(objs, OUT)
+    link([o for f, o in zip(srcs, objs) if os.path.basename(f) not in DEBUG_ONLY], OUT)
     debug_of = dict(zip(debug_src, dbg_objs))
     link([debug_of.get(f, o) for f, o in zip(srcs, objs)], OUT_DEBUG)
     if verbose:

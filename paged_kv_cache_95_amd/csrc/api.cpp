@@ -119,7 +119,15 @@ int32_t pa_debug_checks(void) { return kDebugBuild; }
 
 int pa_debug_take_violation(void* stream, int32_t* code, int64_t* where) {
   if (!code || !where) return PA_ERR_INVALID_ARG;
+#if PA_DEBUG_CHECKS
   return pa::debug_take((hipStream_t)stream, code, where);
+#else
+  // the release build runs no checks, so it never has a violation to report
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return PA_ERR_HIP;
+  *code = 0;
+  *where = 0;
+  return PA_OK;
+#endif
 }
 
 
@@ -374,6 +382,8 @@ int pa_decode_step(void* out, int64_t out_stride_tok, int64_t out_stride_head, c
   PA_DEBUG_GATE(stream);
   PA_DEBUG_CHECK(pa::validate_decode(*pool, block_tables, max_blocks_per_seq, context_lens,
                                      num_seqs, max_context_len, slot_mapping,
+                                     (hipStream_t)stream));
+  PA_DEBUG_CHECK(pa::validate_tokens(*pool, slot_mapping, num_seqs, nullptr, 0,
                                      (hipStream_t)stream));
   return launched(pa::launch_decode_step(*pool, a, rows, (hipStream_t)stream));
 }

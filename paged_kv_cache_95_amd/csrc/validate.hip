@@ -58,14 +58,40 @@ __global__ void __launch_bounds__(64) validate_decode_kernel(
   }
 }
 
+// Slots of one call seen so far, for the duplicate check: open addressing over
+// kDupSlots entries (empty = -1), at most half full (longer calls skip the check).
+constexpr int kDupSlots = 1 << 20;
+constexpr int64_t kDupMaxTokens = kDupSlots / 2;
+static __device__ __align__(16) unsigned long long dup_table[kDupSlots];
+
+__global__ void __launch_bounds__(256) clear_dup_table_kernel(unsigned long long* t) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < kDupSlots; i += gridDim.x * 256) t[i] = ~0ull;
+}
+
+// Insert `slot` (>= 0); true when another token of the call inserted it first.
+__device__ __forceinline__ bool dup_insert(unsigned long long* t, int64_t slot) {
+  const unsigned long long key = (unsigned long long)slot;
+  unsigned h = (unsigned)((key * 0x9E3779B97F4A7C15ull) >> 40) & (kDupSlots - 1);
+  for (int probe = 0; probe < kDupSlots; ++probe) {  // ends: the table is at most half full
+    const unsigned long long prev = atomicCAS(&t[h], ~0ull, key);
+    if (prev == ~0ull) return false;
+    if (prev == key) return true;
+    h = (h + 1) & (kDupSlots - 1);
+  }
+  return false;
+}
+
 // One thread per token: slot_mapping[t] < num_blocks * 16 (negative = padding, legal);
-// with positions, 0 <= positions[t] < max_position.
+// with positions, 0 <= positions[t] < max_position; with `dups`, no slot twice.
 __global__ void __launch_bounds__(256) validate_tokens_kernel(
     const int64_t* __restrict__ slots, int64_t n, int64_t num_blocks,
-    const int64_t* __restrict__ positions, int64_t max_position, unsigned long long* w) {
+    const int64_t* __restrict__ positions, int64_t max_position, unsigned long long* w,
+    unsigned long long* dups) {
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n;
        t += (int64_t)gridDim.x * blockDim.x) {
     if (slots[t] >= num_blocks * kBlockSize) record(w, PA_VIOLATION_SLOT, (uint64_t)t);
+    else if (dups != nullptr && slots[t] >= 0 && dup_insert(dups, slots[t]))
+      record(w, PA_VIOLATION_DUP_SLOT, (uint64_t)t);
     if (positions != nullptr && (positions[t] < 0 || positions[t] >= max_position))
       record(w, PA_VIOLATION_POSITION, (uint64_t)t);
   }
@@ -101,25 +127,32 @@ __global__ void __launch_bounds__(64) validate_varlen_kernel(
       record(w, PA_VIOLATION_BLOCK_ID, seq_block(s, j));
 }
 
-// Device address of the current device's violation word (looked up once per device,
-// with that device current; host code never uses the variable's name as an address).
-static int violation_ptr(unsigned long long** out) {
+// Device addresses of the current device's violation word and duplicate table (looked
+// up once per device, with that device current; host code never uses the variables'
+// names as addresses).
+static int debug_ptrs(unsigned long long** word, unsigned long long** dups) {
   constexpr int kMaxDevices = 64;
   static std::mutex mu;
-  static unsigned long long* ptrs[kMaxDevices] = {};
+  static unsigned long long* words[kMaxDevices] = {};
+  static unsigned long long* tables[kMaxDevices] = {};
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
   if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(mu);
-  if (ptrs[dev] == nullptr) {
+  if (words[dev] == nullptr) {
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(violation_word)) != hipSuccess || p == nullptr)
+    void* t = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(violation_word)) != hipSuccess || p == nullptr ||
+        hipGetSymbolAddress(&t, HIP_SYMBOL(dup_table)) != hipSuccess || t == nullptr)
       return PA_ERR_HIP;
-    ptrs[dev] = (unsigned long long*)p;
+    words[dev] = (unsigned long long*)p;
+    tables[dev] = (unsigned long long*)t;
   }
-  *out = ptrs[dev];
+  *word = words[dev];
+  if (dups != nullptr) *dups = tables[dev];
   return PA_OK;
 }
+static int violation_ptr(unsigned long long** out) { return debug_ptrs(out, nullptr); }
 
 static int read_word(hipStream_t stream, unsigned long long* w_dev, unsigned long long* value) {
   if (hipStreamSynchronize(stream) != hipSuccess) return PA_ERR_HIP;
@@ -168,11 +201,19 @@ int validate_decode(const pa_kv_pool_t& pool, const int32_t* block_tables, int m
 int validate_tokens(const pa_kv_pool_t& pool, const int64_t* slots, int64_t n,
                     const int64_t* positions, int64_t max_position, hipStream_t stream) {
   unsigned long long* w = nullptr;
-  const int st = violation_ptr(&w);
+  unsigned long long* dups = nullptr;
+  const int st = debug_ptrs(&w, &dups);
   if (st != PA_OK) return st;
+  if (n > kDupMaxTokens) {
+    dups = nullptr;  // too many tokens for the table: the duplicate check is skipped
+  } else if (launch_kernel(clear_dup_table_kernel, dim3(1024), dim3(256), stream, dups) !=
+             hipSuccess) {
+    return PA_ERR_HIP;
+  }
   const int64_t grid = std::min<int64_t>((n + 255) / 256, 4096);
   const hipError_t e = launch_kernel(validate_tokens_kernel, dim3((unsigned)grid), dim3(256),
-                                     stream, slots, n, pool.num_blocks, positions, max_position, w);
+                                     stream, slots, n, pool.num_blocks, positions, max_position, w,
+                                     dups);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

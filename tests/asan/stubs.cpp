@@ -39,4 +39,4 @@ int debug_gate(hipStream_t) { reached("debug_gate"); }
 int debug_take(hipStream_t, int32_t*, int64_t*) { reached("debug_take"); }
 }  // namespace pa
 
-extern "C" hipError_t hipGetLastError(void) { reached("hipGetLastError"); }
+extern "C" hipError_t hipStreamSynchronize(hipStream_t) { reached("hipStreamSynchronize"); }

@@ -107,6 +107,19 @@ def test_store_slot_past_the_pool(dev, debug_lib):
     expect_violation("slot", 3)
 
 
+def test_store_slot_named_twice(dev, debug_lib):
+    case = decode_case()
+    s = Setup(case, dev, store_new=False)
+    sl = case.slot_mapping.copy()
+    sl[0] = sl[1] = -1                                # padding twice: legal
+    pa.store_kv(s.pool, s.k_new, s.v_new, torch.from_numpy(sl).to(dev))
+    assert pa.take_violation()[1] == 0
+    sl[3] = sl[2]                                     # two rows into one slot: they race
+    pa.store_kv(s.pool, s.k_new, s.v_new, torch.from_numpy(sl).to(dev))
+    name, code, where = pa.take_violation()
+    assert name == "dup_slot" and where in (2, 3), (name, code, where)
+
+
 def test_decode_step_slot_not_the_new_tokens(dev, debug_lib):
     case = decode_case()
     s = Setup(case, dev, store_new=False)
