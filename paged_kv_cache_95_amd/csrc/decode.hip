@@ -261,18 +261,23 @@ struct ItemIn {
   int bid_lane;
 };
 
-template <int KVT, int D, int G, int QT>
-__device__ __forceinline__ void load_item_inputs(const SplitArgs& a, int s, int split, int g,
-                                                 int lane, ItemIn<KVT, D, G>& in) {
-  using Gm = Geom<KVT, D>;
+// Block id of block `lane` of the split (one per lane, up to 64 blocks).
+__device__ __forceinline__ int item_bid_lane(const SplitArgs& a, int s, int split, int lane) {
   const int jb0 = split * (a.split_tokens / kBlockSize);
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  in.bid_lane = (lane < a.split_tokens / kBlockSize && jb0 + lane < a.max_blocks_per_seq)
-                    ? bt_row[jb0 + lane]
-                    : 0;
+  return (lane < a.split_tokens / kBlockSize && jb0 + lane < a.max_blocks_per_seq)
+             ? bt_row[jb0 + lane]
+             : 0;
+}
+
+// The query rows of heads g*G .. g*G+G-1 of sequence s, in the dot-product body's lane
+// layout.
+template <int KVT, int D, int G, int QT>
+__device__ __forceinline__ void load_item_q(const SplitArgs& a, int s, int g, int lane,
+                                            uint32_t (&qw)[G][Geom<KVT, D>::QW]) {
+  using Gm = Geom<KVT, D>;
   const int t8 = lane & 7;
   const bool k_lane = t8 < Gm::NCH;  // false only for rows shorter than 8 chunks
-  uint32_t (&qw)[G][Gm::QW] = in.qw;
   // ---- query chunks t8 + 8j of the G heads (bf16 pairs, or fp32)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -309,7 +314,108 @@ __device__ __forceinline__ void load_item_inputs(const SplitArgs& a, int s, int 
       }
     }
   }
+}
 
+template <int KVT, int D, int G, int QT>
+__device__ __forceinline__ void load_item_inputs(const SplitArgs& a, int s, int split, int g,
+                                                 int lane, ItemIn<KVT, D, G>& in) {
+  in.bid_lane = item_bid_lane(a, s, split, lane);
+  load_item_q<KVT, D, G, QT>(a, s, g, lane, in.qw);
+}
+
+// Lane roles of the dot-product body for KV head g. Lane l works on DPP row r = l / 16:
+// as a K-lane it holds 16-byte chunk t8 (+ 8j) of tokens tok_k[0..1] of the block, as
+// a V-lane the head dims [cv * D/16, (cv + 1) * D/16) of the row's four tokens tok_v.
+template <int KVT, int D>
+struct DotLanes {
+  int tok_k[2], tok_v[4];
+  uint32_t kofs[2], vofs[4];
+  int t8, cv;
+  bool k_lane;  // false only for rows shorter than 8 chunks
+  __device__ __forceinline__ void init(int hkv, int g, int lane) {
+    using Gm = Geom<KVT, D>;
+    const int r = lane >> 4;
+    const int half = (lane >> 3) & 1;
+    t8 = lane & 7;
+    cv = lane & 15;
+    k_lane = t8 < Gm::NCH;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      tok_k[k] = 8 * k + 2 * r + half;
+      tok_v[2 * k] = tok_k[k];
+      tok_v[2 * k + 1] = 8 * k + 2 * r + (half ^ 1);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) kofs[k] = (uint32_t)((tok_k[k] * hkv + g) * Gm::ROW + t8 * 16);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) vofs[x] = (uint32_t)((tok_v[x] * hkv + g) * Gm::ROW + cv * Gm::VB);
+  }
+};
+
+// Request the K and V rows of pool block bid_raw (the context's tokens first .. first +
+// 15) into b; an id outside the pool reads block 0 and marks no token valid. pnew: the
+// block position of the step's new token (its row is read from krow_new / vrow_new), or
+// outside [0, 16).
+template <int KVT, int D>
+__device__ __forceinline__ void dot_load(const SplitArgs& a, const DotLanes<KVT, D>& ln,
+                                         BlockBuf<KVT, D>& b, int bid_raw, int first, int L,
+                                         int pnew, const char* krow_new,
+                                         const char* vrow_new) {
+  using Gm = Geom<KVT, D>;
+  const int64_t blk_bytes = (int64_t)kBlockSize * a.hkv * Gm::ROW;
+  const bool ok = (unsigned)bid_raw < (uint64_t)a.num_blocks;
+  const int64_t bid = ok ? bid_raw : 0;
+  b.nvalid = ok ? min(kBlockSize, L - first) : 0;
+  const char* kb = a.kpool + bid * blk_bytes;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const char* kp = ln.tok_k[k] == pnew ? krow_new + ln.t8 * 16 : kb + ln.kofs[k];
+#pragma unroll
+    for (int c = 0; c < Gm::KC; ++c) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (ln.k_lane) x = ld_stream16(kp + c * 128);
+      b.k[k][4 * c] = x.x; b.k[k][4 * c + 1] = x.y; b.k[k][4 * c + 2] = x.z;
+      b.k[k][4 * c + 3] = x.w;
+    }
+  }
+  const char* vb = a.vpool + bid * blk_bytes;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    load_dwords<Gm::VW>(ln.tok_v[x] == pnew ? vrow_new + ln.cv * Gm::VB : vb + ln.vofs[x], b.v[x]);
+}
+
+template <int KVT, int D, int G>
+__device__ __forceinline__ void dot_state_init(DecodeState<KVT, D, G>& st) {
+  constexpr float NEG_INF = -__builtin_huge_valf();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = NEG_INF;
+    st.l[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < Geom<KVT, D>::EV; ++e) st.acc[h][e] = 0.0f;
+  }
+}
+
+// Combine the four DPP rows: per head, rescale to the wave max and sum; o = acc / l in
+// lanes 0..15 (lane c: head dims c*D/16 ..), lse2 = log2 of the split's sum of exp2.
+template <int KVT, int D, int G>
+__device__ __forceinline__ void dot_finish(DecodeState<KVT, D, G>& st,
+                                           float (&o)[G][Geom<KVT, D>::EV], float (&lse2)[G]) {
+  using Gm = Geom<KVT, D>;
+  constexpr float NEG_INF = -__builtin_huge_valf();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float M = xor32_max(xor16_max(st.m[h]));
+    const float f = st.m[h] == NEG_INF ? 0.0f : fast_exp2(st.m[h] - M);
+    // l counts this lane's own tokens; the mirrored lane of the row holds the other two
+    const float lr = xor32_sum(xor16_sum((st.l[h] + dpp<kRowMirror>(st.l[h])) * f));
+#pragma unroll
+    for (int e = 0; e < Gm::EV; ++e) st.acc[h][e] = xor32_sum(xor16_sum(st.acc[h][e] * f));
+    const float inv_l = 1.0f / lr;
+    lse2[h] = M + __log2f(lr);
+#pragma unroll
+    for (int e = 0; e < Gm::EV; ++e) o[h][e] = st.acc[h][e] * inv_l;
+  }
 }
 
 // One work item (sequence s, split, kv head g) on one wavefront: the split's partial
@@ -318,15 +424,18 @@ __device__ __forceinline__ void load_item_inputs(const SplitArgs& a, int s, int 
 // past the context (possible in the fused schedule) yields lse2 = -inf.
 // krow_new / vrow_new (may be null): the K / V row of the context's last token taken
 // from the step's input instead of the pool, where a concurrent store is writing it.
-template <int KVT, int D, int G>
+__device__ __forceinline__ void balance_issue(int* progress, int done);
+
+// BALANCE: progress is an LDS array with one entry per wave of an eight-wave workgroup
+// whose waves w and w + 4 run items of equal length (see balance_issue).
+template <int KVT, int D, int G, bool BALANCE = false>
 __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KVT, D, G>& in,
                                              int split, int g, int L, int lane,
                                              float (&o)[G][Geom<KVT, D>::EV], float (&lse2)[G],
                                              const char* krow_new = nullptr,
-                                             const char* vrow_new = nullptr) {
-  using Gm = Geom<KVT, D>;
+                                             const char* vrow_new = nullptr,
+                                             int* progress = nullptr) {
   static_assert(!kQuant<KVT>, "quantised pools take the matrix-core item");
-  constexpr float NEG_INF = -__builtin_huge_valf();
   const int t0 = split * a.split_tokens;
   const int t1 = min(L, t0 + a.split_tokens);
   const int jb0 = t0 / kBlockSize;
@@ -334,69 +443,25 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
   // block loop below is a scalar loop
   const int nblk = __builtin_amdgcn_readfirstlane(t1 > t0 ? (t1 - t0 + kBlockSize - 1) / kBlockSize : 0);
   const int bid_lane = in.bid_lane;
-  const uint32_t (&qw)[G][Gm::QW] = in.qw;
-
-  // ---- lane geometry
-  const int r = lane >> 4;
-  const int half = (lane >> 3) & 1;
-  const int t8 = lane & 7;
-  const int cv = lane & 15;
-  const bool k_lane = t8 < Gm::NCH;  // false only for rows shorter than 8 chunks
-  int tok_k[2], tok_v[4];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    tok_k[k] = 8 * k + 2 * r + half;
-    tok_v[2 * k] = tok_k[k];
-    tok_v[2 * k + 1] = 8 * k + 2 * r + (half ^ 1);
-  }
-
-  const int64_t blk_bytes = (int64_t)kBlockSize * a.hkv * Gm::ROW;
-  uint32_t kofs[2], vofs[4];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) kofs[k] = (uint32_t)((tok_k[k] * a.hkv + g) * Gm::ROW + t8 * 16);
-#pragma unroll
-  for (int x = 0; x < 4; ++x) vofs[x] = (uint32_t)((tok_v[x] * a.hkv + g) * Gm::ROW + cv * Gm::VB);
+  DotLanes<KVT, D> ln;
+  ln.init(a.hkv, g, lane);
 
   auto load = [&](BlockBuf<KVT, D>& b, int j) {
-    const int bid_raw = __builtin_amdgcn_readlane(bid_lane, j);
-    const bool ok = (unsigned)bid_raw < (uint64_t)a.num_blocks;
-    const int64_t bid = ok ? bid_raw : 0;
     const int first = (jb0 + j) * kBlockSize;
-    b.nvalid = ok ? min(kBlockSize, L - first) : 0;
     // position of the step's new token in this block (only the context's last block
     // has one in [0, 16)); lanes holding it read the input row instead of the pool
     const int pnew = krow_new != nullptr ? L - 1 - first : -1;
-    const char* kb = a.kpool + bid * blk_bytes;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const char* kp = tok_k[k] == pnew ? krow_new + t8 * 16 : kb + kofs[k];
-#pragma unroll
-      for (int c = 0; c < Gm::KC; ++c) {
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (k_lane) x = ld_stream16(kp + c * 128);
-        b.k[k][4 * c] = x.x; b.k[k][4 * c + 1] = x.y; b.k[k][4 * c + 2] = x.z;
-        b.k[k][4 * c + 3] = x.w;
-      }
-    }
-    const char* vb = a.vpool + bid * blk_bytes;
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      load_dwords<Gm::VW>(tok_v[x] == pnew ? vrow_new + cv * Gm::VB : vb + vofs[x], b.v[x]);
+    dot_load<KVT, D>(a, ln, b, __builtin_amdgcn_readlane(bid_lane, j), first, L, pnew, krow_new,
+                     vrow_new);
   };
 
   DecodeState<KVT, D, G> st;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    st.m[h] = NEG_INF;
-    st.l[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < Gm::EV; ++e) st.acc[h][e] = 0.0f;
-  }
+  dot_state_init(st);
   auto process = [&](const BlockBuf<KVT, D>& b) {
     if (b.nvalid == kBlockSize)
-      process_block<KVT, D, G, false>(b, st, qw, a.scale_log2, tok_k, tok_v);
+      process_block<KVT, D, G, false>(b, st, in.qw, a.scale_log2, ln.tok_k, ln.tok_v);
     else
-      process_block<KVT, D, G, true>(b, st, qw, a.scale_log2, tok_k, tok_v);
+      process_block<KVT, D, G, true>(b, st, in.qw, a.scale_log2, ln.tok_k, ln.tok_v);
   };
 
   // ring of NB block buffers: block j + NB - 1 is requested before block j is used
@@ -410,33 +475,20 @@ __device__ __forceinline__ void item_partial(const SplitArgs& a, const ItemIn<KV
     for (int p = 0; p < NB - 1; ++p) load(ring[p], min(p, nblk - 1));
     int j0 = 0;
     for (; j0 + NB <= nblk; j0 += NB) {
+      if constexpr (BALANCE) balance_issue(progress, j0);
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         load(ring[(u + NB - 1) % NB], min(j0 + u + NB - 1, nblk - 1));
         process(ring[u]);
       }
     }
+    if constexpr (BALANCE) __builtin_amdgcn_s_setprio(0);
     // fewer than NB blocks left: all of them requested already
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u)
       if (j0 + u < nblk) process(ring[u]);
   }
-
-  // ---- combine the four DPP rows: per head, rescale to the wave max and sum
-  float inv_l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float M = xor32_max(xor16_max(st.m[h]));
-    const float f = st.m[h] == NEG_INF ? 0.0f : fast_exp2(st.m[h] - M);
-    // l counts this lane's own tokens; the mirrored lane of the row holds the other two
-    const float lr = xor32_sum(xor16_sum((st.l[h] + dpp<kRowMirror>(st.l[h])) * f));
-#pragma unroll
-    for (int e = 0; e < Gm::EV; ++e) st.acc[h][e] = xor32_sum(xor16_sum(st.acc[h][e] * f));
-    inv_l[h] = 1.0f / lr;
-    lse2[h] = M + __log2f(lr);
-#pragma unroll
-    for (int e = 0; e < Gm::EV; ++e) o[h][e] = st.acc[h][e] * inv_l[h];
-  }
+  dot_finish(st, o, lse2);
 }
 
 // ---------------------------------------------------------------- matrix-core item
@@ -782,11 +834,59 @@ __device__ __forceinline__ void item_partial_mma(const SplitArgs& a, const MmaIn
 }
 
 // Result of one item in the split-then-merge schedule: the final output row when the
-// sequence has a single split, else the partial in the workspace.
+// sequence has a single split, else the partial in the workspace. o and lse2 as the item
+// bodies leave them (lanes 0..15).
+template <int D, int G, int QT>
+__device__ __forceinline__ void write_item_result(const SplitArgs& a, int s, int split, int g,
+                                                  int nsplit, int lane,
+                                                  const float (&o)[G][D / 16],
+                                                  const float (&lse2)[G]) {
+  constexpr int EV = D / 16;
+  if (lane >= 16) return;
+  const int cv = lane;
+  const int d0 = cv * EV;
+  if (nsplit == 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const int64_t off = (int64_t)s * a.out_st + (int64_t)(g * G + h) * a.out_sh + d0;
+      if constexpr (QT == kF32) {
+#pragma unroll
+        for (int e = 0; e < EV; ++e) ((float*)a.out)[off + e] = o[h][e];
+      } else {
+        uint32_t w[EV / 2];
+#pragma unroll
+        for (int e = 0; e < EV / 2; ++e)
+          w[e] = (uint32_t)f32_to_bf16(o[h][2 * e]) | ((uint32_t)f32_to_bf16(o[h][2 * e + 1]) << 16);
+        uint16_t* op = (uint16_t*)a.out + off;
+        if (a.out_aligned && EV == 8) {
+          *reinterpret_cast<uint4*>(op) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EV / 2; ++e) {
+            op[2 * e] = (uint16_t)w[e];
+            op[2 * e + 1] = (uint16_t)(w[e] >> 16);
+          }
+        }
+      }
+    }
+    return;
+  }
+  const int hq = a.hkv * G;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int64_t row = ((int64_t)s * hq + g * G + h) * a.max_splits + split;
+    float* wo = a.ws_o + row * D + d0;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) wo[e] = o[h][e];
+    if (cv == 0) a.ws_lse[row] = lse2[h];
+  }
+}
+
 template <int KVT, int D, int G, int QT, int NBM = MmaRing<KVT>::value>
 __device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split, int g,
                                             int lane) {
   using Gm = Geom<KVT, D>;
+  static_assert(Gm::EV == D / 16, "one output layout for both item bodies");
   float o[G][Gm::EV], lse2[G];
   int nsplit;
   if constexpr (MmaPath<KVT, G>::value) {
@@ -803,44 +903,7 @@ __device__ __forceinline__ void decode_item(const SplitArgs& a, int s, int split
     nsplit = num_splits(L, a.split_tokens);
     item_partial<KVT, D, G>(a, in, split, g, L, lane, o, lse2);
   }
-  if (lane >= 16) return;
-  const int cv = lane;
-  const int d0 = cv * Gm::EV;
-  if (nsplit == 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int64_t off = (int64_t)s * a.out_st + (int64_t)(g * G + h) * a.out_sh + d0;
-      if constexpr (QT == kF32) {
-#pragma unroll
-        for (int e = 0; e < Gm::EV; ++e) ((float*)a.out)[off + e] = o[h][e];
-      } else {
-        uint32_t w[Gm::EV / 2];
-#pragma unroll
-        for (int e = 0; e < Gm::EV / 2; ++e)
-          w[e] = (uint32_t)f32_to_bf16(o[h][2 * e]) | ((uint32_t)f32_to_bf16(o[h][2 * e + 1]) << 16);
-        uint16_t* op = (uint16_t*)a.out + off;
-        if (a.out_aligned && Gm::EV == 8) {
-          *reinterpret_cast<uint4*>(op) = make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < Gm::EV / 2; ++e) {
-            op[2 * e] = (uint16_t)w[e];
-            op[2 * e + 1] = (uint16_t)(w[e] >> 16);
-          }
-        }
-      }
-    }
-    return;
-  }
-  const int hq = a.hkv * G;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const int64_t row = ((int64_t)s * hq + g * G + h) * a.max_splits + split;
-    float* wo = a.ws_o + row * D + d0;
-#pragma unroll
-    for (int e = 0; e < Gm::EV; ++e) wo[e] = o[h][e];
-    if (cv == 0) a.ws_lse[row] = lse2[h];
-  }
+  write_item_result<D, G, QT>(a, s, split, g, nsplit, lane, o, lse2);
 }
 
 // One work item per wavefront over the full (sequence, max_splits, kv head) range, kv
@@ -924,38 +987,111 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* wave_sums, int& 
 constexpr int kCompactWaves = 8;
 static_assert(kCompactWaves <= kMaxItemWaves && kWaves <= kMaxItemWaves, "decode_item's LDS slices");
 
-template <int KVT, int D, int G, int QT>
-__global__ void __launch_bounds__(64 * kCompactWaves, 1)
-    decode_compact_kernel(SplitArgs a) {
-  __shared__ int cum[kMaxCompactSeqs + 1];  // cum[s] = splits of sequences before s
-  __shared__ int wave_sums[kCompactWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Order in which the persistent schedule hands out the (sequence, split) pairs: every
+// full split first, sequence by sequence, then the sequences' shorter last splits from
+// the longest to the shortest (kLenClasses classes of their block count, each class in
+// sequence order). The shortest items are drawn last, so the workgroups run out of work
+// at about the same time. The order changes no result: each split's partial is computed
+// on its own and the merge takes them in split order.
+// By the whole workgroup: cumf[s] = full splits of the sequences before s (s <=
+// num_seqs), pseq[r] = the sequence of the r-th short split; full = the number of full
+// splits. Returns the number of pairs. Ends with a barrier.
+constexpr int kLenClasses = 8;
+__device__ __forceinline__ int pair_order(const SplitArgs& a, int* cumf, short* pseq,
+                                          int* wave_sums, int& full) {
+  const int spb = a.split_tokens / kBlockSize;  // blocks of a full split
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += 64 * kCompactWaves) {
     const int s = base + (int)threadIdx.x;
-    const int n = s < a.num_seqs ? num_splits(clamped_len(a, s), a.split_tokens) : 0;
+    const int L = s < a.num_seqs ? clamped_len(a, s) : 0;
+    const int n = L > 0 ? L / a.split_tokens : 0;
     int tot;
     const int ex = block_exclusive_scan<kCompactWaves>(n, wave_sums, tot);
-    if (s < a.num_seqs) cum[s] = carry + ex;
+    if (s < a.num_seqs) cumf[s] = carry + ex;
     carry += tot;
   }
-  if (threadIdx.x == 0) cum[a.num_seqs] = carry;
-  __syncthreads();
-  const int64_t entries = (int64_t)carry * a.hkv;
-  const int64_t steps = (entries + kCompactWaves - 1) / kCompactWaves;
-  // the items of workgroup step st (one per wave)
-  auto run_step = [&](int64_t st) {
-    const int64_t e = st * kCompactWaves + wave;
-    if (e >= entries) return;
-    const int g = (int)(e % a.hkv);
-    const int pair = (int)(e / a.hkv);
-    // largest s with cum[s] <= pair (sequences without splits have cum[s] == cum[s+1])
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (cum[mid] <= pair) lo = mid; else hi = mid - 1;
+  if (threadIdx.x == 0) cumf[a.num_seqs] = carry;
+  full = carry;
+  int np = 0;
+  for (int c = 0; c < kLenClasses; ++c) {
+    for (int base = 0; base < a.num_seqs; base += 64 * kCompactWaves) {
+      const int s = base + (int)threadIdx.x;
+      const int L = s < a.num_seqs ? clamped_len(a, s) : 0;
+      const int rem = L > 0 ? L % a.split_tokens : 0;
+      const int nb = (rem + kBlockSize - 1) / kBlockSize;  // 1 .. spb when rem > 0
+      const bool mine = rem > 0 && (spb - nb) * kLenClasses / spb == c;
+      int tot;
+      const int ex = block_exclusive_scan<kCompactWaves>(mine ? 1 : 0, wave_sums, tot);
+      if (mine) pseq[np + ex] = (short)s;
+      np += tot;
     }
-    decode_item<KVT, D, G, QT, 3>(a, lo, pair - cum[lo], g, lane);
+  }
+  __syncthreads();
+  return carry + np;
+}
+
+// Sequence of full split `pair`: the largest s with cum[s] <= pair (sequences without
+// full splits have cum[s] == cum[s + 1]).
+__device__ __forceinline__ int pair_sequence(const int* cum, int num_seqs, int pair) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cum[mid] <= pair) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int KVT, int D, int G, int QT>
+__global__ void __launch_bounds__(64 * kCompactWaves, 1)
+    decode_compact_kernel(SplitArgs a) {
+  __shared__ int cumf[kMaxCompactSeqs + 1];  // see pair_order
+  __shared__ short pseq[kMaxCompactSeqs];
+  __shared__ int wave_sums[kCompactWaves];
+  __shared__ int progress[kCompactWaves];
+  // (a scalar wave index makes the compiler spill the bf16 G = 4 item's registers)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x < kCompactWaves) progress[threadIdx.x] = 0;
+  int full = 0;
+  const int pairs = pair_order(a, cumf, pseq, wave_sums, full);  // ends with a barrier
+  const int64_t entries = (int64_t)pairs * a.hkv;
+  const int64_t steps = (entries + kCompactWaves - 1) / kCompactWaves;
+  // this wave's item of step st: (sequence, split, KV head), or none
+  auto locate = [&](int64_t st, int& sq, int& split, int& g) {
+    const int64_t e = st * kCompactWaves + wave;
+    if (st >= steps || e >= entries) return false;
+    g = (int)(e % a.hkv);
+    const int pair = (int)(e / a.hkv);
+    if (pair < full) {
+      sq = pair_sequence(cumf, a.num_seqs, pair);
+      split = pair - cumf[sq];
+    } else {
+      sq = pseq[pair - full];
+      split = clamped_len(a, sq) / a.split_tokens;  // the last split
+    }
+    sq = __builtin_amdgcn_readfirstlane(sq);
+    split = __builtin_amdgcn_readfirstlane(split);
+    return true;
+  };
+  // the items of workgroup step st (one per wave); the dot-product items of a step have
+  // equal lengths (same sequence and split) when the KV heads are a multiple of eight,
+  // and the issue of each SIMD's two waves is balanced
+  auto run_step = [&](int64_t st) {
+    int sq = 0, split = 0, g = 0;
+    if (!locate(st, sq, split, g)) return;
+    if constexpr (MmaPath<KVT, G>::value) {
+      decode_item<KVT, D, G, QT, 3>(a, sq, split, g, lane);
+    } else {
+      ItemIn<KVT, D, G> in;
+      load_item_inputs<KVT, D, G, QT>(a, sq, split, g, lane, in);
+      const int L = clamped_len(a, sq);
+      float o[G][Geom<KVT, D>::EV], lse2[G];
+      item_partial<KVT, D, G, true>(a, in, split, g, L, lane, o, lse2, nullptr, nullptr,
+                                    progress);
+      write_item_result<D, G, QT>(a, sq, split, g, num_splits(L, a.split_tokens), lane, o,
+                                  lse2);
+      if (lane == 0)
+        __hip_atomic_store(&progress[wave], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
   };
   if (a.counters == nullptr) {
     // no workspace (every context fits one split): the b-th contiguous share of steps
