@@ -380,6 +380,33 @@ def test_many_sequences_use_the_plain_grid(dev):
         check(s, split_tokens=split)
 
 
+def test_longest_first_order_at_the_compact_limit(dev):
+    """The persistent schedule hands out every full split first, then the sequences'
+    shorter last splits longest first (eight classes of block count), keeping the
+    sequence of each short split in a 16-bit LDS table. At its limit of 4096 sequences,
+    with eight KV heads (a step is then the eight heads of one split) and short last
+    splits in every class, sampled sequences match the oracle and, run alone on the
+    single-launch schedule, give the same bits."""
+    B, hq, hkv, D, lmax, split = 4096, 16, 8, 64, 140, 128
+    case = W.random_case(91, B=B, Hq=hq, Hkv=hkv, D=D, lmin=1, lmax=lmax, poison=False)
+    rem = case.context_lens % split
+    nb = (rem[rem > 0] + 15) // 16
+    assert set((split // 16 - nb).tolist()) == set(range(8))  # all eight classes occur
+    s = Setup(case, dev)
+    ws = pa.decode_workspace(B, hq, hkv, D, lmax, split, device=dev)
+    out = pa.decode(s.q, s.pool, s.bt, s.ctx, case.scale, max_context_len=lmax,
+                    split_tokens=split, workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(91)
+    seqs = np.unique(np.concatenate([rng.choice(B, 40, replace=False), [0, B - 1],
+                                     [int(np.argmax(case.context_lens))]]))
+    assert max_err(out[torch.from_numpy(seqs).to(dev)], s.oracle(seqs)) <= TOL["bf16"]
+    for b in seqs[:10].tolist() + [B - 1]:
+        o1 = pa.decode(s.q[b:b + 1], s.pool, s.bt[b:b + 1], s.ctx[b:b + 1], case.scale,
+                       max_context_len=lmax, split_tokens=split, workspace=ws)
+        assert torch.equal(o1[0], out[b]), b
+
+
 def test_skewed_lengths_compact_schedule(dev):
     """Contexts from 1 to 3000 tokens in one batch, many short splits: every
     (sequence, split, kv head) item is visited exactly once by the compact schedule."""
