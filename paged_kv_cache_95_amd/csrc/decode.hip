@@ -1081,14 +1081,37 @@ __global__ void __launch_bounds__(64 * kCompactWaves, 1)
     if constexpr (MmaPath<KVT, G>::value) {
       decode_item<KVT, D, G, QT, 3>(a, sq, split, g, lane);
     } else {
+      using Gm = Geom<KVT, D>;
       ItemIn<KVT, D, G> in;
       load_item_inputs<KVT, D, G, QT>(a, sq, split, g, lane, in);
       const int L = clamped_len(a, sq);
-      float o[G][Geom<KVT, D>::EV], lse2[G];
+      const int nsplit = num_splits(L, a.split_tokens);
+      // Decode step (a.knew set): the wave of the split holding the context's last token
+      // copies that token's K and V rows of its head from the step's input into the
+      // pool before its item's block loads (its query and block-id loads are already
+      // out), then runs the item from the pool. Only this wave reads that row in the
+      // launch, and its block loads follow the copy in the wave's memory order. slot <
+      // 0: no new row, the pool holds the context.
+      if (a.knew != nullptr && split == nsplit - 1) {
+        const int64_t slot = ld_uniform(a.slots + sq);
+        if (slot >= 0 && slot < a.num_blocks * kBlockSize && lane < 2 * Gm::NCH) {
+          // lanes 0 .. NCH-1 copy the K row, the next NCH lanes the V row (16 bytes each)
+          const bool is_v = lane >= Gm::NCH;
+          const int chunk = is_v ? lane - Gm::NCH : lane;
+          const char* src = is_v ? a.vnew + ((int64_t)sq * a.vnew_st + (int64_t)g * a.vnew_sh) * Gm::E
+                                 : a.knew + ((int64_t)sq * a.knew_st + (int64_t)g * a.knew_sh) * Gm::E;
+          const uint4 x = *reinterpret_cast<const uint4*>(src + chunk * 16);
+          const int64_t off = (slot / kBlockSize) * kBlockSize * a.hkv * Gm::ROW +
+                              ((slot % kBlockSize) * a.hkv + g) * Gm::ROW + chunk * 16;
+          *reinterpret_cast<uint4*>(const_cast<char*>(is_v ? a.vpool : a.kpool) + off) = x;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      float o[G][Gm::EV], lse2[G];
       item_partial<KVT, D, G, true>(a, in, split, g, L, lane, o, lse2, nullptr, nullptr,
                                     progress);
-      write_item_result<D, G, QT>(a, sq, split, g, num_splits(L, a.split_tokens), lane, o,
-                                  lse2);
+      write_item_result<D, G, QT>(a, sq, split, g, nsplit, lane, o, lse2);
       if (lane == 0)
         __hip_atomic_store(&progress[wave], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
@@ -1572,7 +1595,9 @@ static int launch_decode_t(const pa_kv_pool_t& pool, const DecodeArgs& a, const 
   // groups) stay below the persistent schedule's two words
   const bool fused = fused_groups <= kFusedMaxWorkgroups &&
                      (sa.max_chunks == 1 || (int64_t)a.num_seqs * pool.kv_heads <= kCompactQueueWord);
-  if (step != nullptr && fused) {
+  // the persistent schedule's dot-product items fold the store in as well
+  const bool fold = fused || (a.num_seqs <= kMaxCompactSeqs && !MmaPath<KVT, G>::value);
+  if (step != nullptr && fold) {
     sa.knew = (const char*)step->k;
     sa.vnew = (const char*)step->v;
     sa.knew_st = step->k_st;

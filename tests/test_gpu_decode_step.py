@@ -52,6 +52,9 @@ CASES = {
     "f32 folded": (dict(seed=62, B=3, Hq=4, Hkv=2, D=64, kv_dtype="f32", lmax=300), 16),
     "fp8 store launch": (dict(seed=63, B=5, Hq=12, Hkv=2, D=128, kv_dtype="fp8", lmax=900), 32),
     "bf16 persistent": (dict(seed=64, B=40, Hq=16, Hkv=4, D=128, kv_dtype="bf16", lmax=3000), 16),
+    "f32 persistent": (dict(seed=69, B=40, Hq=8, Hkv=2, D=64, kv_dtype="f32", lmax=2000), 16),
+    "bf16 persistent matrix cores (store launch)":
+        (dict(seed=70, B=40, Hq=24, Hkv=4, D=128, kv_dtype="bf16", lmax=3000), 16),
 }
 
 
@@ -81,13 +84,15 @@ def test_unaligned_rows_take_the_store_launch(dev):
     assert max_err(out_a, a.oracle()) <= TOL["bf16"]
 
 
-def test_padding_slots_store_nothing(dev):
+@pytest.mark.parametrize("B,Hq,split", [(8, 12, 32), (40, 16, 16)])
+def test_padding_slots_store_nothing(dev, B, Hq, split):
     """Sequences with slot -1 store nothing and attend the pool as it is; the others
-    store and use their new row."""
-    case = W.random_case(67, B=8, Hq=12, Hkv=2, D=128, lmax=1500)
+    store and use their new row (single-launch kernel; persistent kernel with the
+    store folded into its dot-product items)."""
+    case = W.random_case(67, B=B, Hq=Hq, Hkv=2 if Hq == 12 else 4, D=128, lmax=1500)
     sl = torch.from_numpy(case.slot_mapping.copy()).to(dev)
     sl[::3] = -1
-    out_a, a, out_b, b = run_both(case, dev, 32, slots=sl)
+    out_a, a, out_b, b = run_both(case, dev, split, slots=sl)
     assert torch.equal(out_a, out_b)
     assert same_pools(a.pool, b.pool)
 
@@ -119,18 +124,22 @@ def test_step_graph_replay(dev):
         del junk
 
 
-@pytest.mark.parametrize("kv,split", [("bf16", 32), ("fp8", 32), ("bf16", 16)])
-def test_engine_graph_replay_with_in_place_updates(dev, kv, split):
+@pytest.mark.parametrize("kv,split,Hq,long", [("bf16", 32, 12, False), ("fp8", 32, 12, False),
+                                              ("bf16", 16, 12, False), ("bf16", 16, 8, True)])
+def test_engine_graph_replay_with_in_place_updates(dev, kv, split, Hq, long):
     """The engine pattern of a captured decode step: fixed, padded device buffers for q,
     the new K/V rows, slot_mapping, block_tables and context_lens; the step is captured
     once, and before each of ten replays the host writes the next token's values into
     those buffers in place (context_lens += 1, the next slots, one of which crosses into
     a new block every 16 steps for some sequence). Two of the eight batch entries are
     padding: slot -1 and context length 1 on a dummy block. Every replay is checked
-    against the oracle (attention) and the whole pool against the oracle's store."""
+    against the oracle (attention) and the whole pool against the oracle's store.
+    long: one sequence of ~9000 tokens at 16-token splits and G = 4 puts the call on
+    the persistent schedule, whose dot-product items fold the store in."""
     rng = np.random.default_rng(70)
-    B, real, Hq, Hkv, D, nb, steps = 8, 6, 12, 2, 128, 256, 10
-    L0 = np.array([14, 30, 95, 250, 1007, 47], np.int64)          # tokens before step 0
+    B, real, Hkv, D, steps = 8, 6, 2, 128, 10
+    nb = 1024 if long else 256
+    L0 = np.array([14, 30, 95, 250, 9007 if long else 1007, 47], np.int64)  # before step 0
     maxb = int(-(-(L0.max() + steps) // 16))
     perm = rng.permutation(nb - 1).astype(np.int32) + 1          # block 0: the dummy block
     bt = np.full((B, maxb), -1, np.int32)
