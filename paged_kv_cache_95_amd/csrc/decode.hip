@@ -858,9 +858,14 @@ __device__ __forceinline__ void write_item_result(const SplitArgs& a, int s, int
         for (int e = 0; e < EV / 2; ++e)
           w[e] = (uint32_t)f32_to_bf16(o[h][2 * e]) | ((uint32_t)f32_to_bf16(o[h][2 * e + 1]) << 16);
         uint16_t* op = (uint16_t*)a.out + off;
-        if (a.out_aligned && EV == 8) {
-          *reinterpret_cast<uint4*>(op) = make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
+        bool stored = false;
+        if constexpr (EV == 8) {
+          if (a.out_aligned) {
+            *reinterpret_cast<uint4*>(op) = make_uint4(w[0], w[1], w[2], w[3]);
+            stored = true;
+          }
+        }
+        if (!stored) {
 #pragma unroll
           for (int e = 0; e < EV / 2; ++e) {
             op[2 * e] = (uint16_t)w[e];
