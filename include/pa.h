@@ -341,9 +341,11 @@ int pa_decode_noalloc(void *out, int64_t out_stride_tok, int64_t out_stride_head
  * Contract: a slot >= 0 must be the slot of position context_lens[s] - 1 (the new token
  * is the last token of the context). Otherwise the bytes written are still exactly
  * those of pa_store_kv, but that sequence's output is unspecified.
- * For small batches with bf16/fp32 pools and rows starting on 16 bytes, the store is
- * folded into the single decode launch (the new token is read from k_new / v_new while
- * its slot is written); otherwise a store launch runs first. Either way the output and
+ * With bf16/fp32 pools and rows starting on 16 bytes, the store is folded into the
+ * decode launch: small batches read the new token from k_new / v_new while its slot is
+ * written; larger ones (the persistent schedule's dot-product items, at most 4096
+ * sequences, q_heads / kv_heads <= 4 for bf16) store each sequence's row before the
+ * items that read it. Otherwise a store launch runs first. Either way the output and
  * the pool bytes are identical to the two calls. Workspace as for pa_decode.
  */
 int pa_decode_step(void *out, int64_t out_stride_tok, int64_t out_stride_head, const void *q,

@@ -929,11 +929,12 @@ __global__ void __launch_bounds__(64 * kWaves) decode_split_kernel(SplitArgs a) 
   decode_item<KVT, D, G, QT>(a, s, split, g, lane);
 }
 
-// Compact persistent schedule. Every workgroup prefix-sums the per-sequence split
-// counts into LDS, which enumerates exactly the existing (sequence, split, kv head)
-// items (kv head fastest, eight per workgroup step); workgroup b then walks the b-th
-// contiguous share of them. Dispatching only real work matters for skewed batches:
-// padding the grid to max_context_len would launch mostly empty workgroups.
+// Compact persistent schedule. Every workgroup builds, in LDS, the same enumeration of
+// exactly the existing (sequence, split, kv head) items (pair_order; kv head fastest,
+// eight per workgroup step) and draws steps from a device-wide counter (without a
+// workspace: the b-th contiguous share of the steps). Dispatching only real work
+// matters for skewed batches: padding the grid to max_context_len would launch mostly
+// empty workgroups. At most kMaxCompactSeqs sequences (the LDS tables).
 constexpr int kMaxCompactSeqs = 4096;
 
 // The single-launch schedule's workgroup: eight waves, in one unit or two. Quantised
@@ -1059,6 +1060,30 @@ __global__ void __launch_bounds__(64 * kCompactWaves, 1)
   int full = 0;
   const int pairs = pair_order(a, cumf, pseq, wave_sums, full);  // ends with a barrier
   const int64_t entries = (int64_t)pairs * a.hkv;
+  if constexpr (!MmaPath<KVT, G>::value) {
+    if (a.knew != nullptr && blockIdx.x == 0) {
+      // decode step: a sequence without items (context length <= 0, outside the
+      // contract) still gets its new rows stored, as pa_store_kv would store them
+      using Gm = Geom<KVT, D>;
+      for (int sq = (int)threadIdx.x; sq < a.num_seqs; sq += 64 * kCompactWaves) {
+        const int64_t slot = a.slots[sq];
+        if (clamped_len(a, sq) > 0 || slot < 0 || slot >= a.num_blocks * kBlockSize) continue;
+        const int64_t base = (slot / kBlockSize) * kBlockSize * a.hkv * Gm::ROW +
+                             (slot % kBlockSize) * a.hkv * Gm::ROW;
+        for (int g = 0; g < a.hkv; ++g) {
+          const char* kr = a.knew + ((int64_t)sq * a.knew_st + (int64_t)g * a.knew_sh) * Gm::E;
+          const char* vr = a.vnew + ((int64_t)sq * a.vnew_st + (int64_t)g * a.vnew_sh) * Gm::E;
+          for (int c = 0; c < Gm::NCH; ++c) {
+            const int64_t off = base + (int64_t)g * Gm::ROW + c * 16;
+            *reinterpret_cast<uint4*>(const_cast<char*>(a.kpool) + off) =
+                *reinterpret_cast<const uint4*>(kr + c * 16);
+            *reinterpret_cast<uint4*>(const_cast<char*>(a.vpool) + off) =
+                *reinterpret_cast<const uint4*>(vr + c * 16);
+          }
+        }
+      }
+    }
+  }
   const int64_t steps = (entries + kCompactWaves - 1) / kCompactWaves;
   // this wave's item of step st: (sequence, split, KV head), or none
   auto locate = [&](int64_t st, int& sq, int& split, int& g) {

@@ -70,6 +70,27 @@ def test_step_equals_store_then_decode(dev, name):
     assert err <= TOL[case.kv_dtype]
 
 
+def test_persistent_step_stores_rows_of_sequences_without_context(dev):
+    """Outside the contract (context length 0 with a slot): the persistent kernel, whose
+    rows are otherwise stored by each sequence's last split, still writes exactly the
+    bytes pa_store_kv writes; the other sequences' outputs are those of the two calls."""
+    case = W.random_case(72, B=40, Hq=16, Hkv=4, D=128, lmin=1, lmax=3000)
+    bad = [3, 17]
+    a = Setup(case, dev, store_new=False)
+    b = Setup(case, dev, store_new=False)
+    for st in (a, b):
+        st.ctx[bad] = 0
+    out_a = pa.decode_step(a.q, a.pool, a.k_new, a.v_new, a.slots, a.bt, a.ctx, case.scale,
+                           max_context_len=case.max_context_len, split_tokens=16)
+    pa.store_kv(b.pool, b.k_new, b.v_new, b.slots)
+    out_b = pa.decode(b.q, b.pool, b.bt, b.ctx, case.scale,
+                      max_context_len=case.max_context_len, split_tokens=16)
+    torch.cuda.synchronize()
+    assert same_pools(a.pool, b.pool)
+    keep = [i for i in range(40) if i not in bad]
+    assert torch.equal(out_a[keep], out_b[keep])
+
+
 def test_unaligned_rows_take_the_store_launch(dev):
     case = W.random_case(66, B=6, Hq=12, Hkv=2, D=128, lmax=700)
     a0 = Setup(case, dev, store_new=False)
