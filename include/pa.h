@@ -377,7 +377,7 @@ int pa_decode_step(void *out, int64_t out_stride_tok, int64_t out_stride_head, c
  *   cu_seqlens   [num_seqs+1] int32, cu[0] = 0, non-decreasing, cu[num_seqs] =
  *                total_tokens. n_s == 0 is allowed (no rows).
  *   max_q_len    host-side upper bound of n_s (sizes the grid).
- *   split_tokens keys per work item: 0 = 1024, else a positive multiple of 64. A row
+ *   split_tokens keys per work item: 0 = 768, else a positive multiple of 64. A row
  *                tile whose visible keys exceed it is split into key chunks handled
  *                in parallel and merged by log-sum-exp; results depend bitwise only
  *                on this value and each sequence's own (n_s, context_lens[s]).

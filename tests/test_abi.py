@@ -221,6 +221,7 @@ def test_prefill_validation(lib):
     assert prefill(lib, p, split=64, ws=0xE000, wsb=need - 4) == WORKSPACE
     assert prefill(lib, p, split=64, ws=0xE004, wsb=need) == WORKSPACE  # not 16-B aligned
     assert prefill(lib, p, ws=0) == WORKSPACE                  # the work list is needed too
-    assert lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 1024, 0) == plan(10, 12, 1)
-    assert (lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 1025, 0)
+    # split_tokens = 0: 768 keys per item
+    assert lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 768, 0) == plan(10, 12, 1)
+    assert (lib.pa_varlen_prefill_workspace_bytes(10, 12, 128, 769, 0)
             == plan(10, 12, 2) + 10 * 12 * 2 * 129 * 4)
