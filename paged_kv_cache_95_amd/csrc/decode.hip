@@ -1021,10 +1021,15 @@ constexpr int kLenClasses = 8;
 __device__ __forceinline__ int pair_order(const SplitArgs& a, int* cumf, short* pseq,
                                           int* wave_sums, int& full) {
   const int spb = a.split_tokens / kBlockSize;  // blocks of a full split
+  // the first 64 * kCompactWaves lengths are read once and reused by every pass
+  const int L0 = (int)threadIdx.x < a.num_seqs ? clamped_len(a, (int)threadIdx.x) : 0;
+  auto len = [&](int base, int s) {
+    return base == 0 ? L0 : (s < a.num_seqs ? clamped_len(a, s) : 0);
+  };
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += 64 * kCompactWaves) {
     const int s = base + (int)threadIdx.x;
-    const int L = s < a.num_seqs ? clamped_len(a, s) : 0;
+    const int L = len(base, s);
     const int n = L > 0 ? L / a.split_tokens : 0;
     int tot;
     const int ex = block_exclusive_scan<kCompactWaves>(n, wave_sums, tot);
@@ -1037,7 +1042,7 @@ __device__ __forceinline__ int pair_order(const SplitArgs& a, int* cumf, short* 
   for (int c = 0; c < kLenClasses; ++c) {
     for (int base = 0; base < a.num_seqs; base += 64 * kCompactWaves) {
       const int s = base + (int)threadIdx.x;
-      const int L = s < a.num_seqs ? clamped_len(a, s) : 0;
+      const int L = len(base, s);
       const int rem = L > 0 ? L % a.split_tokens : 0;
       const int nb = (rem + kBlockSize - 1) / kBlockSize;  // 1 .. spb when rem > 0
       const bool mine = rem > 0 && (spb - nb) * kLenClasses / spb == c;
