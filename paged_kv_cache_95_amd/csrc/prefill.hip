@@ -41,6 +41,7 @@ constexpr int kPfRows = 128;   // flattened rows per workgroup
 constexpr int kPfKeys = 64;    // keys per iteration
 constexpr int kKPad = 8;       // bf16 elements of padding per K row in LDS
 constexpr int kVPad = 8;       // bf16 elements of padding per V^T row in LDS
+constexpr int kPfORow = 36;    // fp32 LDS row stride of the partial store staging (32 + 4)
 constexpr float kPfLazyMax = 8.0f;  // log2 headroom of the lazily updated row max
 
 __device__ __forceinline__ int vt_pos(int k) {
@@ -101,8 +102,8 @@ __device__ __forceinline__ int pick4(const int (&x)[4], int i) {
 // uniform); Ks / Vt are the workgroup's LDS tiles.
 template <int D, int G>
 __device__ __forceinline__ void prefill_item(const PfArgs& a, uint16_t* __restrict__ Ks,
-                                             uint16_t* __restrict__ Vt, const PfEntry& e,
-                                             int g) {
+                                             uint16_t* __restrict__ Vt, float* __restrict__ Os,
+                                             const PfEntry& e, int g) {
   const uint16_t* __restrict__ kpool = a.kpool;
   const uint16_t* __restrict__ vpool = a.vpool;
   const int64_t num_blocks = a.num_blocks;
@@ -379,26 +380,53 @@ __device__ __forceinline__ void prefill_item(const PfArgs& a, uint16_t* __restri
   }
 
   const float l_tot = xor32_sum(l_run);
-  if (!row_ok) return;
   if (nchunks > 1) {
+    if (!wave_active) return;
     // partial over this key chunk: normalised o and log2-sum-exp; a row that saw no
     // key here (all past its causal limit) gets lse = -inf and weighs nothing
     const bool any = l_tot > 0.0f;
     const float inv = any ? 1.0f / l_tot : 0.0f;
     const int64_t row = ((int64_t)(t_begin + my_tok) * a.q_heads + g * G + my_hh) * a.max_chunks + chunk;
-    float* wo = a.ws_o + row * D;
+    if (row_ok && hl == 0) a.ws_lse[row] = any ? m_run + __log2f(l_tot) : -__builtin_huge_valf();
+    // A lane holds 16-byte pieces of one row, so storing them directly would touch 32
+    // cache lines per instruction. Each 32-wide d slice goes through this wave's LDS
+    // slice instead and leaves as whole 128-byte lines: lane l stores float4 l % 8 of
+    // row 8 i + l / 8 (i = 0..3), eight lanes per line.
+    float* os = Os + wave * (32 * kPfORow);
+    const int rsub = lane >> 3, cq = lane & 7;
+    float* dst[4];
+    bool dst_ok[4];
 #pragma unroll
-    for (int dn = 0; dn < DT; ++dn)
+    for (int i = 0; i < 4; ++i) {
+      const int m = mw0 + 8 * i + rsub;
+      dst_ok[i] = m < nrows;
+      const int mm = dst_ok[i] ? m : mw0;
+      const int64_t r = ((int64_t)(t_begin + mm / G) * a.q_heads + g * G + mm % G) * a.max_chunks + chunk;
+      dst[i] = a.ws_o + r * D + 4 * cq;
+    }
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const int d = 32 * dn + 8 * jq + 4 * hl;
-        *reinterpret_cast<float4*>(wo + d) =
+    for (int dn = 0; dn < DT; ++dn) {
+      // the previous slice's LDS reads are done before this slice overwrites them
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq)
+        *reinterpret_cast<float4*>(&os[l32 * kPfORow + 8 * jq + 4 * hl]) =
             make_float4(oacc[dn][4 * jq] * inv, oacc[dn][4 * jq + 1] * inv,
                         oacc[dn][4 * jq + 2] * inv, oacc[dn][4 * jq + 3] * inv);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(&os[(8 * i + rsub) * kPfORow + 4 * cq]);
+        if (dst_ok[i]) *reinterpret_cast<float4*>(dst[i] + 32 * dn) = v;
       }
-    if (hl == 0) a.ws_lse[row] = any ? m_run + __log2f(l_tot) : -__builtin_huge_valf();
+    }
     return;
   }
+  if (!row_ok) return;
   const float inv = 1.0f / l_tot;
   uint16_t* op = a.out + (int64_t)(t_begin + my_tok) * a.out_st + (int64_t)(g * G + my_hh) * a.out_sh;
 #pragma unroll
@@ -431,6 +459,7 @@ template <int D, int G>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PfArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kPfKeys * (D + kKPad)];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * (kPfKeys + kVPad)];
+  __shared__ __attribute__((aligned(16))) float Os[(kPfRows / 32) * 32 * kPfORow];
   const PfPlanHeader* hdr = reinterpret_cast<const PfPlanHeader*>(a.plan);
   const PfEntry* entries = reinterpret_cast<const PfEntry*>(a.plan + kPfPlanHeaderBytes);
   const int64_t items = (int64_t)hdr->entries * a.hkv;
@@ -440,7 +469,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PfArgs a) {
     if (it >= items) break;
     const int64_t ei = it / a.hkv;
     const PfEntry e = entries[ei];
-    prefill_item<D, G>(a, Ks, Vt, e, (int)(it - ei * a.hkv));
+    prefill_item<D, G>(a, Ks, Vt, Os, e, (int)(it - ei * a.hkv));
   }
 }
 
@@ -571,8 +600,9 @@ __global__ void __launch_bounds__(kPfPlanThreads) prefill_plan_kernel(PfArgs a) 
 
 // Merge of the key-chunk partials. The prefill grid's row tiles are cut into parts of
 // 256 / (D/16) rows; one 256-thread workgroup per (part, row tile, KV head, sequence),
-// one thread per (row, 16-float slice of head_dim), slice fastest so neighbouring
-// threads read neighbouring 64-byte pieces of a partial. Tiles with a single key chunk
+// one thread per (row, slice sl of head_dim), slice fastest. Slice sl holds the four
+// 4-float pieces at d = 4 sl + (D/4) e, e = 0..3, so each load instruction has the
+// D/16 threads of a row read a whole 128-byte line of its partial. Tiles with a single key chunk
 // were written directly by the prefill kernel and their workgroups exit after one load
 // of the sizes. Each thread runs an online log-sum-exp merge over the chunks, loading
 // four chunks ahead.
@@ -620,9 +650,9 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PfArgs a) {
     for (int u = 0; u < U; ++u) {
       const int c = min(c0 + u, nch - 1);
       lse[u] = c0 + u < nch ? a.ws_lse[row0 + c] : NEG_INF;
-      const float4* op = reinterpret_cast<const float4*>(a.ws_o + (row0 + c) * D + sl * 16);
+      const float4* op = reinterpret_cast<const float4*>(a.ws_o + (row0 + c) * D + sl * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[u][e] = op[e];
+      for (int e = 0; e < 4; ++e) o[u][e] = op[e * NS];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -643,19 +673,21 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PfArgs a) {
     }
   }
   const float inv = 1.0f / den;  // chunk 0 always holds key 0, so den > 0
-  uint16_t* dst = a.out + (int64_t)tok * a.out_st + (int64_t)h * a.out_sh + sl * 16;
+  uint16_t* dst = a.out + (int64_t)tok * a.out_st + (int64_t)h * a.out_sh + sl * 4;
   uint32_t w[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
     w[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
   if (a.out_aligned) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) reinterpret_cast<uint2*>(dst)[e] = make_uint2(w[2 * e], w[2 * e + 1]);
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint2*>(dst + e * (D / 4)) = make_uint2(w[2 * e], w[2 * e + 1]);
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      dst[2 * e] = (uint16_t)w[e];
-      dst[2 * e + 1] = (uint16_t)(w[e] >> 16);
+    for (int e = 0; e < 4; ++e) {
+      dst[e * (D / 4)] = (uint16_t)w[2 * e];
+      dst[e * (D / 4) + 1] = (uint16_t)(w[2 * e] >> 16);
+      dst[e * (D / 4) + 2] = (uint16_t)w[2 * e + 1];
+      dst[e * (D / 4) + 3] = (uint16_t)(w[2 * e + 1] >> 16);
     }
   }
 }
