@@ -605,6 +605,15 @@ __device__ __forceinline__ void balance_issue(int* progress, int done) {
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0)
     __hip_atomic_store(&progress[wave], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // At the first ring cycle both waves are at zero: nothing to balance, and the
+  // partner may not have written its entry yet (until it does, LDS holds whatever an
+  // earlier workgroup left there). The partner, started with this wave, writes it
+  // before its first block load, so a later cycle reads a current entry; a late one
+  // would only misplace one cycle's priority.
+  if (done == 0) {
+    __builtin_amdgcn_s_setprio(0);
+    return;
+  }
   // uniform, so that the branch is a scalar one (s_setprio ignores the exec mask)
   const int other = __builtin_amdgcn_readfirstlane(
       __hip_atomic_load(&progress[wave ^ 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));

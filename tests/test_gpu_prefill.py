@@ -121,6 +121,26 @@ def test_empty_chunks_and_strided_q(dev):
     assert max_err(out, s.oracle()) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("split", [0, 64])
+def test_unaligned_out_rows_match_aligned(dev, split):
+    """out starting 2 bytes past an 8-byte boundary takes the element-store paths (the
+    prefill kernel's and, split into 64-key chunks, the merge's): the same bits as an
+    aligned out, and within tolerance of the oracle."""
+    case = W.random_case(26, kind="varlen", B=5, Hq=6, Hkv=2, D=128, lmin=1, lmax=300, nmax=140)
+    s = Setup(case, dev)
+    T, Hq, D = s.q.shape
+    kw = dict(max_q_len=max(1, case.max_q_len), max_context_len=case.max_context_len,
+              split_tokens=split)
+    ref_out = pa.varlen_prefill(s.q, s.cu, s.pool, s.bt, s.ctx, case.scale, **kw)
+    flat = torch.full((T * Hq * D + 1,), float("nan"), dtype=torch.bfloat16, device=dev)
+    out = flat[1:].view(T, Hq, D)
+    assert out.data_ptr() % 8 == 2
+    pa.varlen_prefill(s.q, s.cu, s.pool, s.bt, s.ctx, case.scale, out=out, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert max_err(out, s.oracle()) <= TOL["bf16"]
+
+
 def test_chunked_prefill_equals_one_shot(dev):
     """Prefill of n tokens in one call == the same tokens in two chunks (first chunk,
     then the rest on top of it as cached prefix): chunked prefill on a cached prefix."""
