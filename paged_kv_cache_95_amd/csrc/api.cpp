@@ -437,8 +437,8 @@ int pa_varlen_prefill(void* out, int64_t out_stride_tok, int64_t out_stride_head
     return PA_ERR_WORKSPACE;
   const int64_t tiles = ((int64_t)max_q_len * (q_heads / pool->kv_heads) + 127) / 128;
   const int64_t plan_bound = pa::prefill_plan_bound(total_tokens, q_heads, max_chunks);
-  // work items, the merge grid (at most 4 workgroups per row tile) and the work list
-  if (tiles * std::max(max_chunks, 4) * pool->kv_heads * num_seqs >= (int64_t)1 << 31 ||
+  // work items, the merge grid (at most 8 workgroups per row tile) and the work list
+  if (tiles * std::max(max_chunks, 8) * pool->kv_heads * num_seqs >= (int64_t)1 << 31 ||
       total_tokens * q_heads >= (int64_t)1 << 31 || plan_bound >= (int64_t)1 << 31)
     return PA_ERR_UNSUPPORTED;
 

@@ -598,20 +598,25 @@ __global__ void __launch_bounds__(kPfPlanThreads) prefill_plan_kernel(PfArgs a) 
   }
 }
 
-// Merge of the key-chunk partials. The prefill grid's row tiles are cut into parts of
-// 256 / (D/16) rows; one 256-thread workgroup per (part, row tile, KV head, sequence),
-// one thread per (row, slice sl of head_dim), slice fastest. Slice sl holds the four
-// 4-float pieces at d = 4 sl + (D/4) e, e = 0..3, so each load instruction has the
-// D/16 threads of a row read a whole 128-byte line of its partial. Tiles with a single key chunk
+// Merge of the key-chunk partials. A thread takes kPfMergePieces 4-float pieces of a
+// row: slice sl of the NS = D / (4 kPfMergePieces) slices holds the pieces at
+// d = 4 sl + (D / kPfMergePieces) e, so each load instruction has the NS threads of a row
+// read whole 128-byte lines of its partial. The prefill grid's row tiles are cut into
+// parts of 256 / NS rows; one 256-thread workgroup per (part, row tile, KV head,
+// sequence), one thread per (row, slice), slice fastest. Tiles with a single key chunk
 // were written directly by the prefill kernel and their workgroups exit after one load
 // of the sizes. Each thread runs an online log-sum-exp merge over the chunks, loading
 // four chunks ahead.
+constexpr int kPfMergePieces = 2;
 template <int D>
-constexpr int pf_merge_rows() { return 256 / (D / 16); }
+constexpr int pf_merge_slices() { return D / (4 * kPfMergePieces); }
+template <int D>
+constexpr int pf_merge_rows() { return 256 / pf_merge_slices<D>(); }
 
 template <int D>
 __global__ void __launch_bounds__(256) prefill_merge_kernel(PfArgs a) {
-  constexpr int NS = D / 16;
+  constexpr int E = kPfMergePieces;
+  constexpr int NS = pf_merge_slices<D>();
   constexpr int ROWS = pf_merge_rows<D>();
   constexpr int PARTS = kPfRows / ROWS;
   constexpr float NEG_INF = -__builtin_huge_valf();
@@ -639,20 +644,20 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PfArgs a) {
   const int tok = t_begin + m / G;
   const int h = g * G + m % G;
   const int64_t row0 = ((int64_t)tok * a.q_heads + h) * a.max_chunks;
-  float mx = NEG_INF, den = 0.0f, acc[16];
+  float mx = NEG_INF, den = 0.0f, acc[4 * E];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  for (int e = 0; e < 4 * E; ++e) acc[e] = 0.0f;
   constexpr int U = 4;
   for (int c0 = 0; c0 < nch; c0 += U) {
     float lse[U];
-    float4 o[U][4];
+    float4 o[U][E];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = min(c0 + u, nch - 1);
       lse[u] = c0 + u < nch ? a.ws_lse[row0 + c] : NEG_INF;
       const float4* op = reinterpret_cast<const float4*>(a.ws_o + (row0 + c) * D + sl * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[u][e] = op[e * NS];
+      for (int e = 0; e < E; ++e) o[u][e] = op[e * NS];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -663,7 +668,7 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PfArgs a) {
       const float w = ok ? fast_exp2(lse[u] - m_new) : 0.0f;
       den = ok ? fmaf(den, f, w) : den;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < E; ++e) {
         acc[4 * e] = ok ? fmaf(acc[4 * e], f, w * o[u][e].x) : acc[4 * e];
         acc[4 * e + 1] = ok ? fmaf(acc[4 * e + 1], f, w * o[u][e].y) : acc[4 * e + 1];
         acc[4 * e + 2] = ok ? fmaf(acc[4 * e + 2], f, w * o[u][e].z) : acc[4 * e + 2];
@@ -674,20 +679,20 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PfArgs a) {
   }
   const float inv = 1.0f / den;  // chunk 0 always holds key 0, so den > 0
   uint16_t* dst = a.out + (int64_t)tok * a.out_st + (int64_t)h * a.out_sh + sl * 4;
-  uint32_t w[8];
+  uint32_t w[2 * E];
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
+  for (int e = 0; e < 2 * E; ++e)
     w[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
   if (a.out_aligned) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint2*>(dst + e * (D / 4)) = make_uint2(w[2 * e], w[2 * e + 1]);
+    for (int e = 0; e < E; ++e) *reinterpret_cast<uint2*>(dst + e * (D / E)) = make_uint2(w[2 * e], w[2 * e + 1]);
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dst[e * (D / 4)] = (uint16_t)w[2 * e];
-      dst[e * (D / 4) + 1] = (uint16_t)(w[2 * e] >> 16);
-      dst[e * (D / 4) + 2] = (uint16_t)w[2 * e + 1];
-      dst[e * (D / 4) + 3] = (uint16_t)(w[2 * e + 1] >> 16);
+    for (int e = 0; e < E; ++e) {
+      dst[e * (D / E)] = (uint16_t)w[2 * e];
+      dst[e * (D / E) + 1] = (uint16_t)(w[2 * e] >> 16);
+      dst[e * (D / E) + 2] = (uint16_t)w[2 * e + 1];
+      dst[e * (D / E) + 3] = (uint16_t)(w[2 * e + 1] >> 16);
     }
   }
 }
