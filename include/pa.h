@@ -385,10 +385,14 @@ int pa_decode_step(void *out, int64_t out_stride_tok, int64_t out_stride_head, c
  *                bytes for the same (total_tokens, q_heads, head_dim, max_context_len,
  *                split_tokens); contents on entry ignored. It holds the call's work
  *                list (built on the device from cu_seqlens and context_lens, longest
- *                items first, claimed by persistent workgroups) and, when a row tile's
- *                keys exceed split_tokens, the per-chunk partials. Calls that share a
- *                workspace must be ordered (same stream); overlapping calls race.
+ *                items first, dealt to the persistent workgroups in a fixed order) and,
+ *                when a row tile's keys exceed split_tokens, the per-chunk partials.
+ *                Calls that share a workspace must be ordered (same stream);
+ *                overlapping calls race.
  *   Other arguments as in pa_decode. A chunk of length 1 is a decode row.
+ * Returns PA_ERR_UNSUPPORTED, with nothing launched, when total_tokens * q_heads, the
+ * work-list bound, or the number of work items or merge workgroups (row tiles of 128
+ * flattened rows times max(key chunks, 8) times kv_heads times num_seqs) reaches 2^31.
  * Supported dtypes: (q BF16, pool BF16). QK^T and PV run on the matrix cores with
  * bf16 operands (P rounded to bf16) and fp32 accumulation.
  */
